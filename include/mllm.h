@@ -1,0 +1,235 @@
+/*
+ * mllm.h -- C ABI of the positions-aware cached decode library for MI355X
+ * (gfx950).  ABI version 1.
+ *
+ * The operation (microLLM-rocm ARCHITECTURE.md, "Tensor ownership boundary"):
+ * survivor tokens keep fixed cache-row IDs; device tensors positions[A] and
+ * cache_rows[A] parameterize decode-only RoPE, the K/V store and cached
+ * attention, and inactive full-capacity rows stay untouched.  Equal-length
+ * pending prompts are prefilled as one batch whose prefixes land in empty
+ * shared rows.
+ *
+ * Boundary conventions (ARCHITECTURE.md, "Tensor ownership boundary" and
+ * "Stable integration boundary"):
+ *  - tensors cross as non-owning views: pointer, accessible bytes, shape,
+ *    element strides, dtype and device; the caller keeps ownership;
+ *  - output, workspace, device and stream are explicit; nothing is inferred
+ *    from a pointer; unsupported layouts are rejected, never copied behind the
+ *    caller's back;
+ *  - no entry point throws; each returns an mllm_status and records a
+ *    thread-local message readable through mllm_last_error();
+ *  - every argument check runs before the first HIP call, and a call that
+ *    fails a check has no side effect;
+ *  - the compute calls never allocate, never synchronize and run only on the
+ *    given stream.
+ *
+ * Layouts (all BF16, element strides, innermost dimension contiguous):
+ *  cache K, V : [slots, capacity, H_kv, D] per layer, dense
+ *  decode  q  : [A, H_q, D]      k_new, v_new : [A, H_kv, D]    out : [A, H_q, D]
+ *  prefill q  : [A, T, H_q, D]   k_new, v_new : [A, T, H_kv, D] out : [A, T, H_q, D]
+ * Query head hq reads kv head hq / (H_q / H_kv).
+ */
+#ifndef MLLM_H
+#define MLLM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLLM_ABI_VERSION 1
+
+typedef enum {
+    MLLM_OK = 0,
+    MLLM_ERR_INVALID_ARG = 1,  /* null pointer, bad shape/stride/size, out-of-range index */
+    MLLM_ERR_UNSUPPORTED = 2,  /* dtype, head size or layout this build does not handle */
+    MLLM_ERR_ALIAS = 3,        /* a writable buffer overlaps another argument */
+    MLLM_ERR_OUT_OF_RANGE = 4, /* position or row outside the cache (host mirror check) */
+    MLLM_ERR_ROW_BUSY = 5,     /* prefill target row is not logically empty */
+    MLLM_ERR_WORKSPACE = 6,    /* workspace null or smaller than the *_workspace_size value */
+    MLLM_ERR_OUT_OF_MEMORY = 7,
+    MLLM_ERR_DEVICE = 8        /* a HIP runtime call failed; see mllm_last_error() */
+} mllm_status;
+
+typedef enum { MLLM_BF16 = 1 } mllm_dtype;
+
+/*
+ * Non-owning tensor view ("Tensor ownership boundary": the C ABI builds a
+ * non-owning view from pointer, accessible bytes, shape, element strides,
+ * dtype and device).  Elements [i0..] live at data + sum(i_k * stride[k]) *
+ * element size; every such address must fall inside [data, data + bytes).
+ * Negative dims or strides are rejected.  Zero-size dims are legal.
+ */
+typedef struct {
+    void *data;
+    uint64_t bytes;
+    int32_t ndim;
+    int32_t dtype;     /* mllm_dtype */
+    int32_t device;    /* HIP device ordinal */
+    int32_t reserved;
+    int64_t shape[4];
+    int64_t stride[4]; /* in elements */
+} mllm_tensor_view;
+
+/* Shared slot cache: num_layers x {K, V} x [slots, capacity, h_kv, head_dim]. */
+typedef struct {
+    int32_t num_layers;
+    int32_t slots;
+    int32_t capacity;  /* positions per row: the persistent bound on sequence length */
+    int32_t h_kv;
+    int32_t head_dim;  /* 64 or 128 */
+    int32_t dtype;     /* MLLM_BF16 */
+    int32_t device;
+} mllm_cache_desc;
+
+/* Split-half RoPE over the whole head ("Attention layout boundary"): pairs
+ * (i, i + D/2), angle pos * base^(-2i/D); base must be finite and > 0. */
+typedef struct {
+    double base;
+    int32_t rotary_dim; /* must equal head_dim */
+    int32_t reserved;
+} mllm_rope_desc;
+
+/* Optional knobs of the decode call (NULL = defaults). */
+typedef struct {
+    int32_t keys_per_split; /* 0 = default; else a multiple of 64 in [64, 65536] */
+    int32_t kernel;         /* 0 = tuned split-K kernel, 1 = readable one-wave-per-head kernel */
+    int32_t reserved[6];
+} mllm_decode_opts;
+
+typedef struct mllm_cache mllm_cache; /* opaque */
+
+/* ABI version of the loaded library (MLLM_ABI_VERSION). */
+int mllm_abi_version(void);
+
+/* Thread-local text of the last failure on this thread ("" after success). */
+const char *mllm_last_error(void);
+
+/* Exact device bytes of a cache: num_layers * 2 * slots * capacity * h_kv *
+ * head_dim * 2 ("Tensor ownership boundary": serving runners verify the exact
+ * layer/head/element-size allocation formula). */
+mllm_status mllm_cache_bytes(const mllm_cache_desc *desc, uint64_t *bytes);
+
+/* Allocate an engine-owned cache with hipMalloc on desc->device.  Contents are
+ * not initialized; every row starts logically empty (length 0). */
+mllm_status mllm_cache_alloc(const mllm_cache_desc *desc, mllm_cache **out);
+
+/* Wrap caller-owned device memory (e.g. torch tensors) as a cache.  k_layers
+ * and v_layers hold num_layers pointers, each to a dense [slots, capacity,
+ * h_kv, head_dim] BF16 block, 16-byte aligned.  The caller keeps ownership and
+ * must keep the memory alive until mllm_cache_free. */
+mllm_status mllm_cache_wrap(const mllm_cache_desc *desc, void *const *k_layers,
+                            void *const *v_layers, mllm_cache **out);
+
+/* Release the cache object (and its memory if engine-owned).  NULL is a no-op. */
+mllm_status mllm_cache_free(mllm_cache *cache);
+
+/* Device pointers of one layer's K and V blocks. */
+mllm_status mllm_cache_layer(const mllm_cache *cache, int32_t layer, void **k, void **v);
+
+/* Copy of the descriptor the cache was created with. */
+mllm_status mllm_cache_get_desc(const mllm_cache *cache, mllm_cache_desc *desc);
+
+/* Logical reset of one row ("Tensor ownership boundary": the shared allocation
+ * persists while a finished row's active prefix falls to zero; a reset row is
+ * reused from position zero).  Sets the row length to 0; touches no device
+ * memory. */
+mllm_status mllm_cache_reset_row(mllm_cache *cache, int32_t row);
+
+/* Host-side logical length of one row: T after a prefill, max(len, pos + 1)
+ * after a decode made with a host mirror, 0 after a reset. */
+mllm_status mllm_cache_row_length(const mllm_cache *cache, int32_t row, int32_t *len);
+
+/* Workspace bytes needed by mllm_decode_rope_store_attn for A entries and h_q
+ * query heads.  max_position bounds every position of the call (-1 = capacity
+ * - 1).  opts may be NULL. */
+mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32_t h_q,
+                                       int32_t max_position, const mllm_decode_opts *opts,
+                                       uint64_t *bytes);
+
+/*
+ * One decode step of one layer ("Tensor ownership boundary": device
+ * positions[A] and cache_rows[A] parameterize decode RoPE, the K/V store and
+ * cached attention; inactive rows untouched).  For every a < A, with
+ * p = positions[a], r = cache_rows[a], on `stream`:
+ *   1. K[r, p, h, :] = bf16(RoPE(k_new[a, h, :], p)) and V[r, p, h, :] =
+ *      v_new[a, h, :] (bit copy) for every kv head h; no other cache byte is
+ *      written;
+ *   2. out[a, hq, :] = bf16( softmax_j( RoPE(q[a, hq], p) . K[r, j, hq/G] /
+ *      sqrt(D) ) . V[r, j, hq/G] ) over j = 0..p, the softmax reduced in FP32
+ *      and only the output rounded (operator-development.md, "Public
+ *      interfaces": typed softmax reduces in FP32 registers).
+ *
+ *  q, k_new, v_new : device views, layouts above; D contiguous, 16-byte aligned
+ *                    rows; any non-negative outer strides.
+ *  positions_dev, cache_rows_dev : device int32[A].
+ *  host_mirror     : NULL, or host int32[2*A] = {positions[0..A), rows[0..A)},
+ *                    the same values as the device arrays.  With it the call
+ *                    also rejects out-of-range positions/rows and duplicate
+ *                    rows (MLLM_ERR_OUT_OF_RANGE / MLLM_ERR_INVALID_ARG),
+ *                    sizes the split grid from the largest position, and
+ *                    updates the row lengths.  Without it the kernels skip the
+ *                    store for an out-of-range entry, write NaN to its output
+ *                    and set *status_dev to 1; duplicate rows are then the
+ *                    caller's error (two stores race).
+ *  out             : device view [A, H_q, D]; must not overlap any input,
+ *                    the cache or the workspace (MLLM_ERR_ALIAS).
+ *  workspace       : device buffer of at least mllm_decode_workspace_size()
+ *                    bytes (computed with max_position >= every position, or
+ *                    -1), 256-byte aligned, caller-owned, contents ignored.
+ *  status_dev      : NULL or device int32, set to 1 on a device-side index
+ *                    error, never cleared by the library.
+ *  stream          : hipStream_t (NULL = the null stream).
+ *  A = 0 is a successful no-op.  The call is idempotent (same inputs give the
+ *  same cache bytes and output bits).
+ */
+mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
+                                        const mllm_tensor_view *q,
+                                        const mllm_tensor_view *k_new,
+                                        const mllm_tensor_view *v_new,
+                                        const int32_t *positions_dev,
+                                        const int32_t *cache_rows_dev, int32_t A,
+                                        const int32_t *host_mirror,
+                                        const mllm_rope_desc *rope,
+                                        const mllm_tensor_view *out, void *workspace,
+                                        uint64_t workspace_bytes, int32_t *status_dev,
+                                        const mllm_decode_opts *opts, void *stream);
+
+/* Workspace bytes needed by mllm_prefill_rope_store_attn (may be 0). */
+mllm_status mllm_prefill_workspace_size(const mllm_cache *cache, int32_t A, int32_t T,
+                                        int32_t h_q, uint64_t *bytes);
+
+/*
+ * Equal-length batched prefill of one layer ("Tensor ownership boundary":
+ * equal-length pending prompts run as one batch and each prefix is mapped
+ * into its target empty shared-cache row; different lengths are separate
+ * calls).  For every a < A and t < T, with r = cache_rows[a]:
+ *   K[r, t, h, :] = bf16(RoPE(k_new[a, t, h, :], t)), V[r, t, h, :] = v_new[a, t, h, :];
+ *   out[a, t, hq, :] = causal GQA attention of RoPE(q[a, t, hq], t) over keys
+ *   0..t of row r, FP32 softmax, BF16 output.  The attention products run on
+ *   BF16 matrix cores: the rotated query and the softmax weights are rounded
+ *   to BF16 before each product, accumulation is FP32.
+ * Positions >= T of row r and every other row stay untouched.
+ *
+ *  cache_rows_dev  : device int32[A]; cache_rows_host: host int32[A], the
+ *                    same values (required: rows are checked in range,
+ *                    distinct and logically empty, else MLLM_ERR_ROW_BUSY).
+ *  1 <= T <= capacity.  On success every target row's length becomes T.
+ *  Other arguments as for the decode call.
+ */
+mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
+                                         const mllm_tensor_view *q,
+                                         const mllm_tensor_view *k_new,
+                                         const mllm_tensor_view *v_new,
+                                         const int32_t *cache_rows_dev,
+                                         const int32_t *cache_rows_host, int32_t A, int32_t T,
+                                         const mllm_rope_desc *rope,
+                                         const mllm_tensor_view *out, void *workspace,
+                                         uint64_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLLM_H */

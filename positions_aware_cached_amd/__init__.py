@@ -1,0 +1,261 @@
+"""Python binding of libmllm, the positions-aware cached decode library for MI355X.
+
+Argument marshalling only: every step of the decode and prefill paths runs in
+the library's HIP kernels.  PyTorch supplies device memory and streams; each
+tensor crosses the C ABI (include/mllm.h) as a non-owning view.  The binding
+fails loudly when the library is missing or a call is rejected; there is no
+fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmllm.so")
+
+OK = 0
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIAS", 4: "OUT_OF_RANGE",
+          5: "ROW_BUSY", 6: "WORKSPACE", 7: "OUT_OF_MEMORY", 8: "DEVICE"}
+BF16 = 1
+
+EXPORTS = ("mllm_abi_version", "mllm_last_error", "mllm_cache_bytes", "mllm_cache_alloc",
+           "mllm_cache_wrap", "mllm_cache_free", "mllm_cache_layer", "mllm_cache_get_desc",
+           "mllm_cache_reset_row", "mllm_cache_row_length", "mllm_decode_workspace_size",
+           "mllm_decode_rope_store_attn", "mllm_prefill_workspace_size",
+           "mllm_prefill_rope_store_attn")
+
+
+class MllmError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class TensorView(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("bytes", ctypes.c_uint64), ("ndim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("device", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("shape", ctypes.c_int64 * 4),
+                ("stride", ctypes.c_int64 * 4)]
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("slots", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("device", ctypes.c_int32)]
+
+
+class RopeDesc(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_double), ("rotary_dim", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("keys_per_split", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load libmllm.so (built by positions_aware_cached_amd/build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python positions_aware_cached_amd/build.py`")
+    L = ctypes.CDLL(path)
+    vp, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
+    P = ctypes.POINTER
+    L.mllm_abi_version.restype = ctypes.c_int
+    L.mllm_last_error.restype = ctypes.c_char_p
+    for name in EXPORTS[2:]:
+        getattr(L, name).restype = ctypes.c_int
+    L.mllm_cache_bytes.argtypes = [P(CacheDesc), P(u64)]
+    L.mllm_cache_alloc.argtypes = [P(CacheDesc), P(vp)]
+    L.mllm_cache_wrap.argtypes = [P(CacheDesc), P(vp), P(vp), P(vp)]
+    L.mllm_cache_free.argtypes = [vp]
+    L.mllm_cache_layer.argtypes = [vp, i32, P(vp), P(vp)]
+    L.mllm_cache_get_desc.argtypes = [vp, P(CacheDesc)]
+    L.mllm_cache_reset_row.argtypes = [vp, i32]
+    L.mllm_cache_row_length.argtypes = [vp, i32, P(i32)]
+    L.mllm_decode_workspace_size.argtypes = [vp, i32, i32, i32, P(DecodeOpts), P(u64)]
+    L.mllm_decode_rope_store_attn.argtypes = [
+        vp, i32, P(TensorView), P(TensorView), P(TensorView), vp, vp, i32, P(i32),
+        P(RopeDesc), P(TensorView), vp, u64, vp, P(DecodeOpts), vp]
+    L.mllm_prefill_workspace_size.argtypes = [vp, i32, i32, i32, P(u64)]
+    L.mllm_prefill_rope_store_attn.argtypes = [
+        vp, i32, P(TensorView), P(TensorView), P(TensorView), vp, P(i32), i32, i32,
+        P(RopeDesc), P(TensorView), vp, u64, vp]
+    _lib = L
+    return L
+
+
+def last_error():
+    return load().mllm_last_error().decode()
+
+
+def _check(status):
+    if status != OK:
+        raise MllmError(status, last_error())
+
+
+def view(t):
+    """Non-owning view of a torch tensor (pointer, accessible bytes, shape, strides)."""
+    v = TensorView()
+    if t is None:
+        return None
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"expected a bfloat16 tensor, got {t.dtype}")
+    if t.dim() > 4:
+        raise ValueError("at most 4 dims")
+    v.data = t.data_ptr() if t.numel() else (t.data_ptr() or None)
+    v.bytes = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+    v.ndim = t.dim()
+    v.dtype = BF16
+    v.device = t.device.index if t.is_cuda else -1
+    for i in range(t.dim()):
+        v.shape[i] = t.shape[i]
+        v.stride[i] = t.stride(i)
+    return v
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _opts(keys_per_split=0, kernel=0):
+    o = DecodeOpts()
+    o.keys_per_split = keys_per_split
+    o.kernel = kernel
+    return o
+
+
+def cache_bytes(num_layers, slots, capacity, h_kv, head_dim, device=0):
+    d = CacheDesc(num_layers, slots, capacity, h_kv, head_dim, BF16, device)
+    n = ctypes.c_uint64()
+    _check(load().mllm_cache_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+class Cache:
+    """A shared slot cache: engine-owned (alloc) or wrapping torch tensors (wrap)."""
+
+    def __init__(self, handle, desc, keep=None):
+        self.handle = handle
+        self.desc = desc
+        self._keep = keep  # torch tensors that own wrapped memory
+
+    @classmethod
+    def alloc(cls, num_layers, slots, capacity, h_kv, head_dim, device=0):
+        d = CacheDesc(num_layers, slots, capacity, h_kv, head_dim, BF16, device)
+        h = ctypes.c_void_p()
+        _check(load().mllm_cache_alloc(ctypes.byref(d), ctypes.byref(h)))
+        return cls(h, d)
+
+    @classmethod
+    def wrap(cls, k_layers, v_layers):
+        """Wrap lists of [slots, capacity, h_kv, head_dim] bf16 CUDA tensors (one per layer)."""
+        if len(k_layers) != len(v_layers) or not k_layers:
+            raise ValueError("need the same positive number of K and V layers")
+        t0 = k_layers[0]
+        for t in list(k_layers) + list(v_layers):
+            if t.dtype != torch.bfloat16 or t.shape != t0.shape or not t.is_contiguous():
+                raise ValueError("every layer block must be a contiguous bf16 tensor of one shape")
+        S, C, Hkv, D = t0.shape
+        dev = t0.device.index if t0.is_cuda else -1
+        d = CacheDesc(len(k_layers), S, C, Hkv, D, BF16, dev)
+        n = len(k_layers)
+        ks = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_layers])
+        vs = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_layers])
+        h = ctypes.c_void_p()
+        _check(load().mllm_cache_wrap(ctypes.byref(d), ks, vs, ctypes.byref(h)))
+        return cls(h, d, keep=(list(k_layers), list(v_layers)))
+
+    def free(self):
+        if self.handle:
+            _check(load().mllm_cache_free(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+    def layer_ptrs(self, layer):
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(load().mllm_cache_layer(self.handle, layer, ctypes.byref(k), ctypes.byref(v)))
+        return k.value, v.value
+
+    def reset_row(self, row):
+        _check(load().mllm_cache_reset_row(self.handle, row))
+
+    def row_length(self, row):
+        n = ctypes.c_int32()
+        _check(load().mllm_cache_row_length(self.handle, row, ctypes.byref(n)))
+        return n.value
+
+
+def decode_workspace_size(cache, A, h_q, max_position=-1, keys_per_split=0, kernel=0):
+    n = ctypes.c_uint64()
+    o = _opts(keys_per_split, kernel)
+    _check(load().mllm_decode_workspace_size(cache.handle, A, h_q, max_position,
+                                             ctypes.byref(o), ctypes.byref(n)))
+    return n.value
+
+
+def decode_rope_store_attn(cache, layer, q, k_new, v_new, positions, rows, out, workspace,
+                           base, host_mirror=None, status=None, keys_per_split=0, kernel=0,
+                           stream=None):
+    """One decode step of one layer (see mllm_decode_rope_store_attn in include/mllm.h).
+
+    q [A,Hq,D], k_new/v_new [A,Hkv,D], out [A,Hq,D]: bf16 CUDA tensors.
+    positions, rows: int32 CUDA tensors [A].  workspace: uint8 CUDA tensor.
+    host_mirror: optional int32 CPU tensor/array of 2*A (positions then rows).
+    """
+    A = q.shape[0]
+    rope = RopeDesc(float(base), q.shape[-1], 0)
+    o = _opts(keys_per_split, kernel)
+    hm = None
+    if host_mirror is not None:
+        hm_t = torch.as_tensor(host_mirror, dtype=torch.int32).contiguous()
+        hm = ctypes.cast(hm_t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().mllm_decode_rope_store_attn(
+        cache.handle, layer, ctypes.byref(view(q)), ctypes.byref(view(k_new)),
+        ctypes.byref(view(v_new)), _ptr(positions), _ptr(rows), A, hm, ctypes.byref(rope),
+        ctypes.byref(view(out)), ws_ptr, ws_bytes, _ptr(status), ctypes.byref(o),
+        _stream(stream)))
+
+
+def prefill_workspace_size(cache, A, T, h_q):
+    n = ctypes.c_uint64()
+    _check(load().mllm_prefill_workspace_size(cache.handle, A, T, h_q, ctypes.byref(n)))
+    return n.value
+
+
+def prefill_rope_store_attn(cache, layer, q, k_new, v_new, rows_dev, rows_host, out, workspace,
+                            base, stream=None):
+    """Equal-length prefill of one layer (see mllm_prefill_rope_store_attn)."""
+    A, T = q.shape[0], q.shape[1]
+    rope = RopeDesc(float(base), q.shape[-1], 0)
+    rh = torch.as_tensor(rows_host, dtype=torch.int32).contiguous()
+    _check(load().mllm_prefill_rope_store_attn(
+        cache.handle, layer, ctypes.byref(view(q)), ctypes.byref(view(k_new)),
+        ctypes.byref(view(v_new)), _ptr(rows_dev),
+        ctypes.cast(rh.data_ptr(), ctypes.POINTER(ctypes.c_int32)), A, T, ctypes.byref(rope),
+        ctypes.byref(view(out)), _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))

@@ -1,0 +1,67 @@
+// kernels.h -- internal launch interface between the host layer (mllm.cpp)
+// and the gfx950 kernels (decode.hip, prefill.hip).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace mllm {
+
+constexpr int kMaxHalfDim = 64;  // D / 2 for the largest supported head size (128)
+
+// Everything one decode step needs, resolved and validated by the host layer.
+struct DecodeParams {
+    const uint16_t *q;      // [A, Hq, D] bf16, strides q_sa / q_sh (elements)
+    const uint16_t *k_new;  // [A, Hkv, D]
+    const uint16_t *v_new;  // [A, Hkv, D]
+    int64_t q_sa, q_sh, kn_sa, kn_sh, vn_sa, vn_sh;
+    const int32_t *positions;  // [A] device
+    const int32_t *rows;       // [A] device
+    uint16_t *kc;              // layer K block [S, C, Hkv, D], dense
+    uint16_t *vc;              // layer V block
+    uint16_t *out;             // [A, Hq, D]
+    int64_t o_sa, o_sh;
+    float *qrot;      // workspace [A, Hq, D]      rotated queries, FP32
+    float *part_o;    // workspace [A, Hq, NS, D]  per-split unnormalized outputs
+    float *part_ml;   // workspace [A, Hq, NS, 2]  per-split (max, sum) in the log2 domain
+    int32_t *status;  // optional device status word
+    int32_t A, S, C, Hq, Hkv, D, G;
+    int32_t NS;        // splits per row in the grid
+    int32_t kps;       // keys per split
+    float scale_log2;  // log2(e) / sqrt(D)
+    float inv_freq[kMaxHalfDim];
+};
+
+// Workspace carve-up for a decode step (all offsets 256-byte aligned).
+struct DecodeWorkspace {
+    uint64_t qrot_off, part_o_off, part_ml_off, total;
+};
+DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t D, int64_t NS);
+
+// RoPE(K) + K/V store + RoPE(Q) -> qrot.  One block per active entry.
+hipError_t launch_rope_store(const DecodeParams &p, hipStream_t stream);
+// Tuned split-K attention: per-split partials into the workspace.
+hipError_t launch_decode_split(const DecodeParams &p, hipStream_t stream);
+// Cross-split merge -> BF16 output.
+hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream);
+// Readable one-wave-per-(entry, query head) attention straight to the output.
+hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream);
+
+struct PrefillParams {
+    const uint16_t *q;      // [A, T, Hq, D]
+    const uint16_t *k_new;  // [A, T, Hkv, D]
+    const uint16_t *v_new;  // [A, T, Hkv, D]
+    int64_t q_sa, q_st, q_sh, kn_sa, kn_st, kn_sh, vn_sa, vn_st, vn_sh;
+    const int32_t *rows;    // [A] device
+    uint16_t *kc, *vc;      // layer blocks [S, C, Hkv, D]
+    uint16_t *out;          // [A, T, Hq, D]
+    int64_t o_sa, o_st, o_sh;
+    uint16_t *qrot;         // workspace [A, Hq, T, D] bf16 rotated queries (head-major)
+    int32_t A, T, S, C, Hq, Hkv, D, G;
+    float scale_log2;
+    float inv_freq[kMaxHalfDim];
+};
+uint64_t prefill_workspace_bytes(int64_t A, int64_t T, int64_t Hq, int64_t D);
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
+
+}  // namespace mllm

@@ -1,0 +1,239 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol declared in
+include/mllm.h, and rejects every invalid argument before its first HIP call
+(fake device pointers are safe here: no check reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import positions_aware_cached_amd as pac
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mllm.h")
+
+FAKE = 0x7F0000000000  # 256-aligned fake device address, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mllm_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = pac.load()
+    names = declared_functions()
+    assert "mllm_decode_rope_store_attn" in names and "mllm_prefill_rope_store_attn" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(pac.EXPORTS)
+
+
+def test_abi_version():
+    assert pac.load().mllm_abi_version() == 1
+
+
+def test_cache_bytes_formula():
+    # L * 2 * S * C * Hkv * D * 2 bytes
+    assert pac.cache_bytes(1, 64, 4096, 8, 128) == 1 * 2 * 64 * 4096 * 8 * 128 * 2
+    assert pac.cache_bytes(32, 256, 8192, 8, 128) == 32 * 2 * 256 * 8192 * 8 * 128 * 2
+    for bad in [(0, 1, 1, 1, 64), (1, 0, 1, 1, 64), (1, 1, 0, 1, 64), (1, 1, 1, 0, 64)]:
+        with pytest.raises(pac.MllmError) as e:
+            pac.cache_bytes(*bad)
+        assert e.value.name == "INVALID_ARG"
+    with pytest.raises(pac.MllmError) as e:
+        pac.cache_bytes(1, 1, 1, 1, 96)
+    assert e.value.name == "UNSUPPORTED"
+
+
+def fake_view(shape, addr=FAKE, strides=None, dtype=pac.BF16, device=0, nbytes=None):
+    v = pac.TensorView()
+    v.data = addr
+    v.ndim = len(shape)
+    v.dtype = dtype
+    v.device = device
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    n = 1
+    for s in shape:
+        n *= s
+    v.bytes = nbytes if nbytes is not None else n * 2
+    for i, (s, st) in enumerate(zip(shape, strides)):
+        v.shape[i] = s
+        v.stride[i] = st
+    return v
+
+
+class FakeCache:
+    """A cache wrapping fake device addresses (wrap makes no HIP call)."""
+
+    def __init__(self, L=2, S=8, C=256, Hkv=2, D=64):
+        self.S, self.C, self.Hkv, self.D = S, C, Hkv, D
+        lb = S * C * Hkv * D * 2
+        self.k = [FAKE + 0x100000000 * (2 * l + 1) for l in range(L)]
+        self.v = [FAKE + 0x100000000 * (2 * l + 2) for l in range(L)]
+        d = pac.CacheDesc(L, S, C, Hkv, D, pac.BF16, 0)
+        ks = (ctypes.c_void_p * L)(*self.k)
+        vs = (ctypes.c_void_p * L)(*self.v)
+        h = ctypes.c_void_p()
+        st = pac.load().mllm_cache_wrap(ctypes.byref(d), ks, vs, ctypes.byref(h))
+        assert st == 0, pac.last_error()
+        self.cache = pac.Cache(h, d)
+        self.lb = lb
+
+
+def call_decode(fc, A=4, Hq=4, q=None, k=None, v=None, out=None, pos=FAKE + 0x10000,
+                rows=FAKE + 0x20000, mirror=None, base=1e4, rotary=None, ws=FAKE + 0x40000000,
+                ws_bytes=1 << 30, layer=0, opts=None, status=None):
+    D = fc.D
+    q = q or fake_view([A, Hq, D], FAKE + 0x1000000)
+    k = k or fake_view([A, fc.Hkv, D], FAKE + 0x2000000)
+    v = v or fake_view([A, fc.Hkv, D], FAKE + 0x3000000)
+    out = out or fake_view([A, Hq, D], FAKE + 0x4000000)
+    rope = pac.RopeDesc(base, D if rotary is None else rotary, 0)
+    hm = None
+    if mirror is not None:
+        hm = (ctypes.c_int32 * len(mirror))(*mirror)
+    o = opts or pac.DecodeOpts()
+    return pac.load().mllm_decode_rope_store_attn(
+        fc.cache.handle, layer, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+        ctypes.c_void_p(pos), ctypes.c_void_p(rows), A, hm, ctypes.byref(rope),
+        ctypes.byref(out), ctypes.c_void_p(ws), ws_bytes, ctypes.c_void_p(status),
+        ctypes.byref(o), None)
+
+
+def expect(st, name):
+    assert pac.STATUS[st] == name, (pac.STATUS[st], pac.last_error())
+    assert pac.last_error()
+
+
+def test_decode_rejections_before_device():
+    fc = FakeCache()
+    D = fc.D
+    expect(call_decode(fc, layer=2), "INVALID_ARG")
+    expect(call_decode(fc, A=-1), "INVALID_ARG")
+    expect(call_decode(fc, Hq=3, q=fake_view([4, 3, D], FAKE + 0x1000000),
+                       out=fake_view([4, 3, D], FAKE + 0x4000000)), "INVALID_ARG")
+    expect(call_decode(fc, Hq=34, q=fake_view([4, 34, D], FAKE + 0x1000000),
+                       out=fake_view([4, 34, D], FAKE + 0x4000000)), "UNSUPPORTED")  # G = 17
+    expect(call_decode(fc, base=0.0), "INVALID_ARG")
+    expect(call_decode(fc, base=float("inf")), "INVALID_ARG")
+    expect(call_decode(fc, rotary=32), "UNSUPPORTED")
+    # views
+    expect(call_decode(fc, q=fake_view([4, 4, D], dtype=7)), "UNSUPPORTED")
+    expect(call_decode(fc, q=fake_view([4, 4, D], FAKE + 0x1000000, device=1)), "INVALID_ARG")
+    expect(call_decode(fc, k=fake_view([4, 1, D], FAKE + 0x2000000)), "INVALID_ARG")
+    expect(call_decode(fc, q=fake_view([4, 4, D], FAKE + 0x1000000, strides=[4 * D, D, 2])),
+           "UNSUPPORTED")   # D not contiguous
+    expect(call_decode(fc, q=fake_view([4, 4, D], FAKE + 0x1000000, strides=[4 * D, 4, 1])),
+           "UNSUPPORTED")   # head stride not a multiple of 8
+    expect(call_decode(fc, q=fake_view([4, 4, D], FAKE + 0x1000000, strides=[-4 * D, D, 1])),
+           "INVALID_ARG")   # negative stride
+    expect(call_decode(fc, q=fake_view([4, 4, D], FAKE + 0x1000002)), "UNSUPPORTED")  # misaligned
+    expect(call_decode(fc, q=fake_view([4, 4, D], FAKE + 0x1000000, nbytes=4 * 4 * D * 2 - 2)),
+           "INVALID_ARG")   # view exceeds its storage
+    expect(call_decode(fc, q=fake_view([4, 4, D], 0)), "INVALID_ARG")                 # null data
+    expect(call_decode(fc, pos=0), "INVALID_ARG")
+    # workspace
+    expect(call_decode(fc, ws=0), "WORKSPACE")
+    expect(call_decode(fc, ws=FAKE + 0x40000010), "WORKSPACE")
+    expect(call_decode(fc, ws_bytes=16), "WORKSPACE")
+    # options
+    o = pac.DecodeOpts()
+    o.keys_per_split = 100
+    expect(call_decode(fc, opts=o), "INVALID_ARG")
+    o.keys_per_split, o.kernel = 0, 5
+    expect(call_decode(fc, opts=o), "INVALID_ARG")
+
+
+def test_decode_alias_rejections():
+    fc = FakeCache()
+    D = fc.D
+    # out overlapping q
+    expect(call_decode(fc, out=fake_view([4, 4, D], FAKE + 0x1000000 + 256)), "ALIAS")
+    # out inside the cache K block of the layer
+    expect(call_decode(fc, out=fake_view([4, 4, D], fc.k[0] + 4096)), "ALIAS")
+    # workspace overlapping the V block
+    expect(call_decode(fc, ws=fc.v[0] + 0x100), "ALIAS")
+    # status word inside the output
+    expect(call_decode(fc, status=FAKE + 0x4000000 + 8), "ALIAS")
+    # read-only inputs may overlap each other (k_new and v_new the same memory)
+    st = call_decode(fc, mirror=[1, 2, 3, 300, 0, 1, 2, 3],
+                     v=fake_view([4, fc.Hkv, D], FAKE + 0x2000000))
+    expect(st, "OUT_OF_RANGE")  # got past the alias check to the mirror check
+
+
+def test_decode_host_mirror_rejections():
+    fc = FakeCache()
+    expect(call_decode(fc, mirror=[1, 2, 3, 256, 0, 1, 2, 3]), "OUT_OF_RANGE")   # pos >= C
+    expect(call_decode(fc, mirror=[1, 2, 3, -1, 0, 1, 2, 3]), "OUT_OF_RANGE")
+    expect(call_decode(fc, mirror=[1, 2, 3, 4, 0, 1, 2, 8]), "OUT_OF_RANGE")     # row >= S
+    expect(call_decode(fc, mirror=[1, 2, 3, 4, 0, 1, 2, 2]), "INVALID_ARG")      # duplicate row
+
+
+def test_decode_zero_entries_is_noop():
+    fc = FakeCache()
+    st = call_decode(fc, A=0, ws=0, ws_bytes=0)
+    assert st == 0, pac.last_error()
+
+
+def test_workspace_size_and_rows():
+    fc = FakeCache()
+    a = pac.decode_workspace_size(fc.cache, 4, 4, -1, keys_per_split=64)
+    b = pac.decode_workspace_size(fc.cache, 4, 4, 10, keys_per_split=64)
+    assert a > b > 0
+    with pytest.raises(pac.MllmError):
+        pac.decode_workspace_size(fc.cache, 4, 3, -1)
+    with pytest.raises(pac.MllmError):
+        pac.decode_workspace_size(fc.cache, 4, 4, fc.C)
+    assert fc.cache.row_length(3) == 0
+    fc.cache.reset_row(3)
+    with pytest.raises(pac.MllmError) as e:
+        fc.cache.reset_row(fc.S)
+    assert e.value.name == "OUT_OF_RANGE"
+    k, v = fc.cache.layer_ptrs(1)
+    assert (k, v) == (fc.k[1], fc.v[1])
+    with pytest.raises(pac.MllmError):
+        fc.cache.layer_ptrs(2)
+
+
+def test_wrap_rejections():
+    d = pac.CacheDesc(1, 2, 16, 1, 64, pac.BF16, 0)
+    h = ctypes.c_void_p()
+    L = pac.load()
+    ks = (ctypes.c_void_p * 1)(FAKE)
+    vs = (ctypes.c_void_p * 1)(FAKE + 64)     # overlaps K block
+    expect(L.mllm_cache_wrap(ctypes.byref(d), ks, vs, ctypes.byref(h)), "ALIAS")
+    vs = (ctypes.c_void_p * 1)(FAKE + 0x100008)
+    expect(L.mllm_cache_wrap(ctypes.byref(d), ks, vs, ctypes.byref(h)), "UNSUPPORTED")
+    vs = (ctypes.c_void_p * 1)(0)
+    expect(L.mllm_cache_wrap(ctypes.byref(d), ks, vs, ctypes.byref(h)), "INVALID_ARG")
+
+
+def call_prefill(fc, A=2, T=16, Hq=4, rows_host=(0, 1), ws=FAKE + 0x40000000, ws_bytes=1 << 30,
+                 q=None, out=None):
+    D = fc.D
+    q = q or fake_view([A, T, Hq, D], FAKE + 0x1000000)
+    k = fake_view([A, T, fc.Hkv, D], FAKE + 0x2000000)
+    v = fake_view([A, T, fc.Hkv, D], FAKE + 0x3000000)
+    out = out or fake_view([A, T, Hq, D], FAKE + 0x4000000)
+    rope = pac.RopeDesc(1e4, D, 0)
+    rh = (ctypes.c_int32 * max(1, len(rows_host)))(*rows_host)
+    return pac.load().mllm_prefill_rope_store_attn(
+        fc.cache.handle, 0, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+        ctypes.c_void_p(FAKE + 0x20000), rh, A, T, ctypes.byref(rope), ctypes.byref(out),
+        ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_prefill_rejections_before_device():
+    fc = FakeCache()
+    expect(call_prefill(fc, T=0, q=fake_view([2, 0, 4, fc.D])), "INVALID_ARG")
+    expect(call_prefill(fc, T=fc.C + 1), "INVALID_ARG")
+    expect(call_prefill(fc, rows_host=(0, 0)), "INVALID_ARG")
+    expect(call_prefill(fc, rows_host=(0, 9)), "OUT_OF_RANGE")
+    expect(call_prefill(fc, ws=0), "WORKSPACE")
+    expect(call_prefill(fc, out=fake_view([2, 16, 4, fc.D], FAKE + 0x1000000)), "ALIAS")
