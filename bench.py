@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Decode-step throughput of the positions-aware cached decode path on one MI355X.
+
+One step = one layer of the whole hot path on one batch of synthetic input:
+RoPE(K) + K/V store into the shared slot cache, RoPE(Q), split-K causal GQA
+attention over every row's prefix, cross-split merge to the BF16 output.
+Steps rotate over several layer caches (as a multi-layer decode does), so a
+step never finds its K/V bytes left in the 256 MB last-level cache by the
+previous step.
+
+Prints one JSON line: KV GB/s (algorithmic K+V prefix bytes per step / step
+time), % of the 8 TB/s HBM peak, tokens/s, the dominant kernel's roofline
+point (its own duration from HIP events the library records around it), and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published
+METRIC = "decode attn step: KV GB/s and % of HBM peak; tokens/s at A rows, ctx"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "ragged", "long"])
+    ap.add_argument("--layers", type=int, default=8, help="layer caches rotated over the steps")
+    ap.add_argument("--keys-per-split", type=int, default=0)
+    ap.add_argument("--kernel", type=int, default=0, help="0 tuned split-K, 1 readable")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU-oracle sample (0 = skip)")
+    return ap.parse_args()
+
+
+def hip_runtime():
+    """The HIP runtime torch loaded (one runtime per process)."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                L = ctypes.CDLL(line.split()[-1])
+                L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+                L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                  ctypes.c_void_p, ctypes.c_void_p]
+                L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+                L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+                return L
+    raise RuntimeError("HIP runtime not loaded")
+
+
+def percentile(xs, q):
+    """Linear-interpolation percentile (numpy's default rule)."""
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path runs on one GPU, rows shard across GPUs with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import positions_aware_cached_amd as pac
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workloads.config(args.workload)
+    A, S, C, Hq, Hkv, D = (cfg[k] for k in ("A", "S", "C", "Hq", "Hkv", "D"))
+    print(f"[bench] drawing {args.workload} inputs + {args.layers} layer caches", file=sys.stderr,
+          flush=True)
+    inp = workloads.draw_decode(cfg, device="cuda")
+    layers = [(inp["Kc"], inp["Vc"])] + workloads.draw_cache_layers(cfg, args.layers - 1)
+    cache = pac.Cache.wrap([k for k, _ in layers], [v for _, v in layers])
+    pos_h, rows_h = inp["positions"], inp["rows"]
+    pos = torch.as_tensor(pos_h, device=dev)
+    rows = torch.as_tensor(rows_h, device=dev)
+    out = torch.empty((A, Hq, D), dtype=torch.bfloat16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    mirror = np.concatenate([pos_h, rows_h]).astype(np.int32)
+    nws = pac.decode_workspace_size(cache, A, Hq, int(pos_h.max()), args.keys_per_split,
+                                    args.kernel)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    call = pac.DecodeCall(cache, inp["q"], inp["k_new"], inp["v_new"], pos, rows, out, ws,
+                          cfg["base"], host_mirror=mirror, status=status,
+                          keys_per_split=args.keys_per_split, kernel=args.kernel)
+
+    # algorithmic bytes of one step
+    ctx = pos_h.astype(np.int64) + 1
+    kv_bytes = int(ctx.sum()) * Hkv * D * 2 * 2
+    io_bytes = A * Hq * D * 2 * 2 + 2 * A * Hkv * D * 2 * 2 + 8 * A
+    total_bytes = kv_bytes + io_bytes
+
+    hip = hip_runtime()
+    K, W, L = args.steps, args.warmup, args.layers
+    evs = []
+    for _ in range(K):
+        pair = (ctypes.c_void_p * 2)()
+        for j in range(2):
+            h = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(h)) == 0
+            pair[j] = h.value
+        evs.append(pair)
+
+    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    for i in range(W):
+        call(i % L)
+    torch.cuda.synchronize()
+    # timed region: K steps; the library stamps the attention kernel's own
+    # start/end into the events through its dispatch (no extra queue commands)
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        call(i % L, attn_events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(status.item()) == 0, "device reported an index error"
+    attn_ms = []
+    for pair in evs:
+        f = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(pair[0]),
+                                       ctypes.c_void_p(pair[1])) == 0
+        attn_ms.append(f.value)
+        hip.hipEventDestroy(ctypes.c_void_p(pair[0]))
+        hip.hipEventDestroy(ctypes.c_void_p(pair[1]))
+    # per-step distribution from a separate untimed pass (events between steps
+    # add queue commands, so they stay out of the timed region)
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(min(K, 100))]
+    for i, (e0, e1) in enumerate(step_ev):
+        e0.record()
+        call(i % L)
+        e1.record()
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
+
+    ms_per_step = wall * 1e3 / K
+    kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    tot_gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
+    attn_avg = float(np.mean(attn_ms))
+    attn_gbs = kv_bytes / (attn_avg * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}_decode", "A": A, "slots": S, "capacity": C,
+                   "h_q": Hq, "h_kv": Hkv, "head_dim": D, "rope_base": cfg["base"],
+                   "ctx_mean": round(float(ctx.mean()), 1), "ctx_max": int(ctx.max()),
+                   "layers_rotated": L, "keys_per_split": args.keys_per_split or 256,
+                   "kernel": "fused split-k" if args.kernel == 0 else "readable"},
+        "pct_hbm_peak": round(100.0 * tot_gbs / PEAK_HBM_GBS, 2),
+        "total_gbs": round(tot_gbs, 1),
+        "tokens_per_s": round(A / (ms_per_step * 1e-3), 1),
+        "step_ms_median": round(percentile(step_ms, 50), 4),
+        "step_ms_p95": round(percentile(step_ms, 95), 4),
+        "kv_bytes_per_step": kv_bytes,
+        "total_bytes_per_step": total_bytes,
+        "roofline": {
+            "kernel": "k_decode_fused" if args.kernel == 0 else "k_decode_readable",
+            "bound": "hbm",
+            "achieved": round(attn_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "avg_launch_ms": round(attn_avg, 5),
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+
+    if args.cpu_seconds > 0:
+        call(0)  # a fresh layer-0 step: the oracle sample is compared with it
+        torch.cuda.synchronize()
+        res["cpu_baseline"] = cpu_baseline(args, cfg, inp, layers[0], pos_h, rows_h, out)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(args, cfg, inp, layer0, pos_h, rows_h, out_gpu):
+    """The CPU oracle (single thread, as it stands) on a bounded sample of the
+    same workload: entries one by one, each on a host copy of its row's prefix,
+    until the time budget is spent.  Its outputs are also compared with the
+    GPU's layer-0 outputs for those entries."""
+    import torch
+
+    import oracle
+    import workloads
+
+    Kc, Vc = layer0
+    Hkv, D = cfg["Hkv"], cfg["D"]
+    qb, kb, vb = (workloads.bits(inp[k]) for k in ("q", "k_new", "v_new"))
+    orc = oracle.default()
+    done, kv, elapsed, worst = 0, 0, 0.0, 0.0
+    t_start = time.perf_counter()
+    for a in range(len(pos_h)):
+        p, r = int(pos_h[a]), int(rows_h[a])
+        Km = workloads.bits(Kc[r, :p + 1]).reshape(1, p + 1, Hkv, D).copy()
+        Vm = workloads.bits(Vc[r, :p + 1]).reshape(1, p + 1, Hkv, D).copy()
+        t0 = time.perf_counter()
+        o = orc.decode_step(qb[a:a + 1], kb[a:a + 1], vb[a:a + 1], [p], [0], Km, Vm, cfg["base"])
+        elapsed += time.perf_counter() - t0
+        done += 1
+        kv += (p + 1) * Hkv * D * 2 * 2
+        g = workloads.bits(out_gpu[a])
+        worst = max(worst, float(np.abs(oracle.bf16_to_f32(o[0]).astype(np.float64) -
+                                        oracle.bf16_to_f32(g).astype(np.float64)).max()))
+        if elapsed >= args.cpu_seconds or time.perf_counter() - t_start > 3 * args.cpu_seconds:
+            break
+    del torch
+    return {"value": round(kv / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(pos_h)} entries of the {args.workload} decode step "
+                      f"(layer 0), {kv} KV bytes, {elapsed:.2f} s single-threaded",
+            "tokens_per_s": round(done / elapsed, 3),
+            "gpu_vs_oracle_max_abs": worst}
+
+
+if __name__ == "__main__":
+    main()

@@ -95,7 +95,12 @@ typedef struct {
 typedef struct {
     int32_t keys_per_split; /* 0 = default; else a multiple of 64 in [64, 65536] */
     int32_t kernel;         /* 0 = tuned split-K kernel, 1 = readable one-wave-per-head kernel */
-    int32_t reserved[6];
+    /* NULL, or a hipEvent_t[2] that the call records on its stream right before
+     * and right after the attention kernel (the split-K kernel, or the readable
+     * kernel), for per-kernel timing attribution (operator-development.md,
+     * "Public interfaces": Event timing attributed per layer). */
+    void *attn_events;
+    int32_t reserved[4];
 } mllm_decode_opts;
 
 typedef struct mllm_cache mllm_cache; /* opaque */

@@ -54,7 +54,7 @@ class RopeDesc(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("keys_per_split", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("attn_events", ctypes.c_void_p), ("reserved", ctypes.c_int32 * 4)]
 
 
 _lib = None
@@ -134,10 +134,12 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _opts(keys_per_split=0, kernel=0):
+def _opts(keys_per_split=0, kernel=0, attn_events=None):
     o = DecodeOpts()
     o.keys_per_split = keys_per_split
     o.kernel = kernel
+    if attn_events is not None:
+        o.attn_events = ctypes.cast(attn_events, ctypes.c_void_p)
     return o
 
 
@@ -217,16 +219,18 @@ def decode_workspace_size(cache, A, h_q, max_position=-1, keys_per_split=0, kern
 
 def decode_rope_store_attn(cache, layer, q, k_new, v_new, positions, rows, out, workspace,
                            base, host_mirror=None, status=None, keys_per_split=0, kernel=0,
-                           stream=None):
+                           attn_events=None, stream=None):
     """One decode step of one layer (see mllm_decode_rope_store_attn in include/mllm.h).
 
     q [A,Hq,D], k_new/v_new [A,Hkv,D], out [A,Hq,D]: bf16 CUDA tensors.
     positions, rows: int32 CUDA tensors [A].  workspace: uint8 CUDA tensor.
     host_mirror: optional int32 CPU tensor/array of 2*A (positions then rows).
+    attn_events: optional ctypes array of two hipEvent_t handles recorded around
+    the attention kernel.
     """
     A = q.shape[0]
     rope = RopeDesc(float(base), q.shape[-1], 0)
-    o = _opts(keys_per_split, kernel)
+    o = _opts(keys_per_split, kernel, attn_events)
     hm = None
     if host_mirror is not None:
         hm_t = torch.as_tensor(host_mirror, dtype=torch.int32).contiguous()
@@ -259,3 +263,39 @@ def prefill_rope_store_attn(cache, layer, q, k_new, v_new, rows_dev, rows_host, 
         ctypes.byref(view(out)), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream)))
+
+
+class DecodeCall:
+    """A decode call with every argument marshalled once (for tight loops).
+
+    The tensors must stay alive and unchanged in shape while the object is
+    used; `__call__(layer)` issues one decode step of that layer on `stream`.
+    """
+
+    def __init__(self, cache, q, k_new, v_new, positions, rows, out, workspace, base,
+                 host_mirror=None, status=None, keys_per_split=0, kernel=0, stream=None):
+        self.L = load()
+        self.cache = cache
+        self._keep = (q, k_new, v_new, positions, rows, out, workspace, status)
+        self.A = q.shape[0]
+        self.vq, self.vk, self.vv, self.vo = view(q), view(k_new), view(v_new), view(out)
+        self.rope = RopeDesc(float(base), q.shape[-1], 0)
+        self.opts = _opts(keys_per_split, kernel)
+        self.hm_t = None
+        self.hm = None
+        if host_mirror is not None:
+            self.hm_t = torch.as_tensor(host_mirror, dtype=torch.int32).contiguous()
+            self.hm = ctypes.cast(self.hm_t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+        self.args_tail = (_ptr(positions), _ptr(rows), self.A, self.hm, ctypes.byref(self.rope),
+                          ctypes.byref(self.vo), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _ptr(status))
+        self.stream = _stream(stream)
+
+    def __call__(self, layer, attn_events=None):
+        self.opts.attn_events = (ctypes.cast(attn_events, ctypes.c_void_p).value
+                                 if attn_events is not None else None)
+        st = self.L.mllm_decode_rope_store_attn(
+            self.cache.handle, layer, ctypes.byref(self.vq), ctypes.byref(self.vk),
+            ctypes.byref(self.vv), *self.args_tail, ctypes.byref(self.opts), self.stream)
+        if st != OK:
+            raise MllmError(st, last_error())

@@ -4,27 +4,29 @@
 // device positions[A] and cache_rows[A] parameterize decode RoPE, the K/V
 // store and cached attention; rows not named in cache_rows stay untouched.
 //
-// Kernels, launched in this order on one stream:
-//   k_rope_store      one block per entry: split-half RoPE of k_new stored as
-//                     BF16 at (row, pos), v_new copied bit for bit, rotated
-//                     queries kept in FP32 in the workspace.
-//   k_decode_split    one wave per (entry, kv head, key split): scores on the
-//                     matrix cores, online FP32 softmax, FP32 P.V, per-split
-//                     partial (max, sum, unnormalized output).
+// Tuned path, two launches on one stream:
+//   k_decode_fused    one wave per (entry, kv head, key split): RoPE of the
+//                     queries, RoPE(K) + K/V store by the split that holds the
+//                     new position, scores and P.V on the matrix cores, online
+//                     FP32 softmax, per-split partial (max, sum, unnormalized
+//                     output) into the workspace;
 //   k_decode_merge    one wave per (entry, query head): rescales and sums the
 //                     split partials (the streaming-attention merge of the
 //                     IPU refactor log, "Flash vs materialized attention"),
 //                     divides, rounds to BF16.
-//   k_decode_readable the plain reference-level kernel (one wave per
-//                     (entry, query head), one key at a time), kept for
-//                     diagnosis as the operator workflow asks
-//                     (operator-development.md, "Acceptance rule").
+// Readable path (reference level, kept for diagnosis as the operator workflow
+// asks -- operator-development.md, "Acceptance rule"):
+//   k_rope_store      one block per entry: RoPE(K) + K/V store, rotated
+//                     queries in FP32 into the workspace;
+//   k_decode_readable one wave per (entry, query head), one key at a time.
 //
 // Numerics: the softmax runs in the log2 domain (scores pre-multiplied by
 // log2(e)/sqrt(D), exp2), every sum is FP32, only the output is rounded.
-// On the matrix cores the FP32 rotated query enters as the exact sum of three
-// BF16 parts (hi + mid + lo == q exactly), so each product q_d * k_d is exact
-// and accumulates in FP32: no rounding of the query is introduced.
+// On the matrix cores the FP32 rotated query and the FP32 softmax weights
+// enter as sums of BF16 parts (see Cols below), so the products are those of
+// the FP32 values (exactly for up to 4 query heads per kv head, to 2^-16
+// relative beyond) and accumulate in FP32.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -165,212 +167,381 @@ __global__ __launch_bounds__(64) void k_decode_readable(DecodeParams p)
         out[lane + 64 * e] = (uint16_t)f2bf(o[e] / l);
 }
 
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
 // ---------------------------------------------------------------- R3
 //
-// One wave per (entry a, kv head h, split s).  The split's keys are visited in
-// tiles of 32.  Per tile:
-//   QK on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = 16 keys x 32
-//      dims of K (lane l: key l%16, dims 8*(l/16)..+7 of the k-step, loaded
-//      straight from the cache row), B = 32 dims x 16 columns of the rotated
-//      query, column n = query head n of the group; the three BF16 parts of
-//      the FP32 query accumulate into one FP32 tile.  Lane l then holds the
-//      scores of keys 4*(l/16)+i, i < 4, for head l%16.
-//   softmax: tile max per head across the four row groups, running max,
-//      exp2, running sum; the weights go through LDS as p[key][head].
-//   PV on the vector ALUs in FP32: lane l owns 8 dims (l % (D/8)) of one key
-//      slot (l / (D/8)); V rows are read coalesced along D (16 B per lane).
-template <int D, int GP>
-__global__ __launch_bounds__(64) void k_decode_split(DecodeParams p)
+// k_decode_fused: one wave per (entry a, kv head h, key split s).
+//
+// Prologue: cos/sin of the entry's position (one pair index per lane, in
+// double, rounded once); the wave rotates its G query heads itself.  The wave
+// that owns the split holding position pos also rotates k_new, stores K' and
+// V into (row, pos) and patches its own LDS copy of that key, so the key it
+// attends to is exactly the stored one.
+//
+// Key tiles of 16: while tile t is computed from LDS, tile t+1 is in flight in
+// registers (K in matrix-core operand order, V in row order, 16 B per lane).
+//   QK  v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims of K, B = 32 dims x
+//       16 columns holding the BF16 parts of the FP32 rotated query heads;
+//       lane l ends with the scores of keys 4*(l/16)+i for column l%16.
+//   softmax per column in FP32 (exp2 on log2(e)/sqrt(D)-scaled scores),
+//       running max / sum across tiles.
+//   PV  v_mfma_f32_16x16x16bf16_1k: A = V^T (16 dims x 16 keys) read with
+//       ds_read_b64_tr_b16 from the row-major LDS tile, B = the BF16 parts of
+//       the FP32 weights in the same columns; FP32 accumulators O^T[d][col].
+//
+// Operand columns: part q (hi / mid / lo BF16 part) of head g sits in column
+// q*GS + g (GCLS <= 8, one column group) or column g of group q (GCLS 16).
+// Three parts reproduce an FP32 value exactly (GCLS <= 4); two parts carry
+// it to 2^-16 relative (GCLS 8, 16).
+template <int GCLS>
+struct Cols {
+    static constexpr int GS = GCLS;
+    static constexpr int NPART = GCLS <= 4 ? 3 : 2;
+    static constexpr int NGRP = GCLS == 16 ? 2 : 1;
+};
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+// 2^x for x <= HEADROOM or -inf (the softmax weights): the hardware exp2.
+// Its result for arguments below -126 is flushed to zero, which only drops
+// weights under 2^-126 of the running maximum.
+__device__ __forceinline__ float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// BF16 part `part` of x: with three parts hi + mid + lo == x exactly (each
+// remainder is exact and the last has at most 8 significant bits); with two
+// parts the remainder is rounded to nearest.
+template <int NPART>
+__device__ __forceinline__ uint32_t bf16_part(float x, int part)
 {
-    constexpr int KS = D / 32;      // MFMA k-steps over the head dimension
-    constexpr int LPK = D / 8;      // lanes per key in the P.V layout
-    constexpr int KPS = 64 / LPK;   // keys per P.V step
-    constexpr int TK = 32;          // keys per tile
-    constexpr int NBLK = TK / 16;   // 16-key MFMA blocks per tile
-    constexpr int NST = TK / KPS;   // P.V steps per tile
+    const uint32_t hi = __float_as_uint(x) & 0xffff0000u;
+    if (part == 0)
+        return hi >> 16;
+    const float r1 = x - __uint_as_float(hi);
+    if (NPART == 2)
+        return f2bf(r1);
+    const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
+    if (part == 1)
+        return mid >> 16;
+    const float r2 = r1 - __uint_as_float(mid);
+    return __float_as_uint(r2) >> 16;
+}
+
+#ifndef MLLM_DECODE_WAVES_PER_SIMD
+#define MLLM_DECODE_WAVES_PER_SIMD 2
+#endif
+template <int D, int GCLS>
+__global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) void k_decode_fused(DecodeParams p)
+{
+    using CL = Cols<GCLS>;
+    constexpr int GS = CL::GS, NPART = CL::NPART, NGRP = CL::NGRP;
+    constexpr int KS = D / 32;             // QK k-steps (32 dims each)
+    constexpr int NDB = D / 16;            // PV dim blocks (16 dims each)
+    constexpr int TK = 32;                 // keys per tile
+    constexpr int NB = TK / 16;            // 16-key MFMA row blocks per tile
+    constexpr int LPK = D / 8;             // lanes per key row (16 B each)
+    constexpr int KPI = 64 / LPK;          // key rows per V load instruction
+    constexpr int VLD = TK / KPI;          // V load instructions per tile
+    constexpr int VROW = D * 2 + 16;       // padded LDS row of V, bytes
+    constexpr float HEADROOM = 8.0f;       // log2 growth of a column max before O is rescaled
 
     const int s = blockIdx.x, h = blockIdx.y, a = blockIdx.z;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x, n = lane & 15, lg = lane >> 4;
     const int pos = p.positions[a], row = p.rows[a];
-    if (!entry_valid(p, pos, row))
+    const int G = p.G;
+    if (!entry_valid(p, pos, row)) {
+        if (s == 0 && h == 0 && lane == 0 && p.status)
+            p.status[0] = 1;
         return;
+    }
     const int nkeys = pos + 1;
     const int j0 = s * p.kps;
     if (j0 >= nkeys)
         return;
     const int j1 = min(nkeys, j0 + p.kps);
-    const int G = p.G;
 
-    __shared__ float p_lds[TK * GP];
-    __shared__ float alpha_lds[GP];
+    __shared__ float cs[D / 2], sn[D / 2];
+    __shared__ __attribute__((aligned(16))) unsigned char klds[TK * D * 2];
+    __shared__ __attribute__((aligned(16))) unsigned char vlds[TK * VROW];
+    __shared__ __attribute__((aligned(16))) uint16_t newk[D], newv[D];  // the new token
 
-    const int n = lane & 15, grp = lane >> 4;
+    const size_t slot = (size_t)p.Hkv * D;
+    const size_t rbase = (size_t)row * p.C * slot + (size_t)h * D;
+    const unsigned char *kb = (const unsigned char *)(p.kc + rbase);
+    const unsigned char *vb = (const unsigned char *)(p.vc + rbase);
+    const uint32_t slotb = (uint32_t)(slot * 2);  // bytes per position; a row fits in 2^31
 
-    // B operands: three BF16 parts of the rotated query, column n = head n.
-    bf16x8 bq[3][KS];
-    {
-        const float *qr = p.qrot + ((size_t)a * p.Hq + (size_t)h * G + n) * D;
-        const bool live = n < G;
+    // ---- tile staging: registers (in flight) -> LDS (computed)
+    u32x4 kn[NB][KS], vn[VLD];
+    auto load_tile = [&](int jt) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 w[3];
+        for (int b = 0; b < NB; ++b) {
+            const uint32_t off = (uint32_t)min(jt + b * 16 + n, j1 - 1) * slotb + lg * 16;
 #pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-                uint32_t b0[3], b1[3];
+            for (int ks = 0; ks < KS; ++ks)
+                kn[b][ks] = *(const u32x4 *)(kb + off + ks * 64);
+        }
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const float x = live ? qr[ks * 32 + grp * 8 + j + half] : 0.0f;
-                    const uint32_t hi = __float_as_uint(x) & 0xffff0000u;
-                    const float r1 = x - __uint_as_float(hi);
-                    const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
-                    const float r2 = r1 - __uint_as_float(mid);
-                    const uint32_t lo = __float_as_uint(r2) & 0xffff0000u;
-                    uint32_t *dst = half ? b1 : b0;
-                    dst[0] = hi >> 16;
-                    dst[1] = mid >> 16;
-                    dst[2] = lo >> 16;
-                }
-#pragma unroll
-                for (int part = 0; part < 3; ++part)
-                    w[part][j / 2] = b0[part] | (b1[part] << 16);
-            }
-#pragma unroll
-            for (int part = 0; part < 3; ++part)
-                bq[part][ks] = __builtin_bit_cast(bf16x8, w[part]);
+        for (int i = 0; i < VLD; ++i) {
+            const uint32_t off = (uint32_t)min(jt + i * KPI + lane / LPK, j1 - 1) * slotb +
+                                 (lane % LPK) * 16;
+            vn[i] = *(const u32x4 *)(vb + off);
+        }
+    };
+    load_tile(j0);  // first tile in flight during the prologue below
+
+    if (lane < D / 2) {
+        const float theta = __fmul_rn((float)pos, p.inv_freq[lane]);
+        cs[lane] = (float)cos((double)theta);
+        sn[lane] = (float)sin((double)theta);
+    }
+    __syncthreads();
+
+
+    // ---- the new token: rotate k_new, store K' and V (split holding pos only)
+    const bool owner = j1 == nkeys;
+    if (owner) {
+        if (lane < D / 2) {
+            const uint16_t *k = p.k_new + a * p.kn_sa + h * p.kn_sh;
+            float lo, hi;
+            rope_pair(bf2f(k[lane]), bf2f(k[lane + D / 2]), cs[lane], sn[lane], lo, hi);
+            const uint16_t klo = (uint16_t)f2bf(lo), khi = (uint16_t)f2bf(hi);
+            uint16_t *kd = p.kc + rbase + (size_t)pos * slot;
+            kd[lane] = klo;
+            kd[lane + D / 2] = khi;
+            newk[lane] = klo;
+            newk[lane + D / 2] = khi;
+        }
+        if (lane < LPK) {
+            const u32x4 v = *(const u32x4 *)(p.v_new + a * p.vn_sa + h * p.vn_sh + lane * 8);
+            *(u32x4 *)(p.vc + rbase + (size_t)pos * slot + lane * 8) = v;
+            *(u32x4 *)(newv + lane * 8) = v;
         }
     }
 
-    const size_t slot = (size_t)p.Hkv * D;
-    const uint16_t *kbase = p.kc + (size_t)row * p.C * slot + (size_t)h * D;
-    const uint16_t *vbase = p.vc + (size_t)row * p.C * slot + (size_t)h * D;
-    const int kq = lane / LPK, dc = lane % LPK;
+    // ---- B operands of QK: BF16 parts of the rotated query, by column
+    bf16x8 bq[NGRP][KS];
+    const int chead = NGRP == 1 ? n % GS : n;   // head of this lane's column
+    const int cpart = NGRP == 1 ? n / GS : 0;   // part of this lane's column (one group)
+    const bool ccol = chead < G && (NGRP == 2 || cpart < NPART);
+    {
+        float qv[KS][8];
+        const uint16_t *qs = p.q + a * p.q_sa + (h * G + (ccol ? chead : 0)) * p.q_sh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 w = *(const u32x4 *)(qs + ks * 32 + lg * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qv[ks][2 * e] = bf_lo(w[e]);
+                qv[ks][2 * e + 1] = bf_hi(w[e]);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = ks * 32 + lg * 8 + j;
+                float lo, hi;
+                rope_pair(qv[ks][j], qv[ks + KS / 2][j], cs[i], sn[i], lo, hi);
+                qv[ks][j] = lo;
+                qv[ks + KS / 2][j] = hi;
+            }
+#pragma unroll
+        for (int c = 0; c < NGRP; ++c) {
+            const int part = NGRP == 1 ? min(cpart, NPART - 1) : c;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t b0 = ccol ? bf16_part<NPART>(qv[ks][2 * e], part) : 0u;
+                    const uint32_t b1 = ccol ? bf16_part<NPART>(qv[ks][2 * e + 1], part) : 0u;
+                    w[e] = b0 | (b1 << 16);
+                }
+                bq[c][ks] = __builtin_bit_cast(bf16x8, w);
+            }
+        }
+    }
 
-    float m_run = -INFINITY, l_run = 0.0f;
-    float o[GP][8];
+    auto store_tile = [&](int jt) {
 #pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            o[g][e] = 0.0f;
-
-    for (int jt = j0; jt < j1; jt += TK) {
-        u32x4 kreg[NBLK][KS];
-        u32x4 vreg[NST];
-#pragma unroll
-        for (int b = 0; b < NBLK; ++b) {
-            const int key = min(jt + b * 16 + n, j1 - 1);
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kreg[b][ks] = *(const u32x4 *)(kbase + (size_t)key * slot + ks * 32 + grp * 8);
-        }
+                *(u32x4 *)(klds + (b * KS + ks) * 1024 + lane * 16) = kn[b][ks];
 #pragma unroll
-        for (int st = 0; st < NST; ++st) {
-            const int key = min(jt + st * KPS + kq, j1 - 1);
-            vreg[st] = *(const u32x4 *)(vbase + (size_t)key * slot + dc * 8);
+        for (int i = 0; i < VLD; ++i)
+            *(u32x4 *)(vlds + (i * KPI + lane / LPK) * VROW + (lane % LPK) * 16) = vn[i];
+        if (owner && pos >= jt && pos < jt + TK) {
+            // the key just stored: overwrite the stale copy that was loaded
+            const int kk = pos - jt, b = kk >> 4, m = kk & 15;
+            if (lane < LPK) {
+                // 16-B chunk c = lane of the key: K operand slot (ks, lg) = (c / 4, c % 4)
+                *(u32x4 *)(klds + (b * KS + (lane >> 2)) * 1024 + (m + 16 * (lane & 3)) * 16) =
+                    *(const u32x4 *)(newk + lane * 8);
+                *(u32x4 *)(vlds + kk * VROW + lane * 16) = *(const u32x4 *)(newv + lane * 8);
+            }
+            // keys past pos were clamped to pos and hold its stale bytes: they
+            // carry zero weight, so give them zero values (0 * stale NaN = NaN)
+            for (int idx = lane; idx < (TK - 1 - kk) * LPK; idx += 64)
+                *(u32x4 *)(vlds + (kk + 1 + idx / LPK) * VROW + (idx % LPK) * 16) =
+                    u32x4{0u, 0u, 0u, 0u};
         }
+    };
 
-        // scores
-        float sc[NBLK][4];
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 O[NGRP][NDB];
+#pragma unroll
+    for (int c = 0; c < NGRP; ++c)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            O[c][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    store_tile(j0);
+    __syncthreads();
+    for (int jt = j0; jt < j1; jt += TK) {
+        const bool more = jt + TK < j1;
+        if (more)
+            load_tile(jt + TK);
+
+        // QK: lane (n, lg) gets keys jt + 16 b + 4 lg + i of column n
+        f32x4 acc[NB][NGRP];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int c = 0; c < NGRP; ++c)
+                acc[b][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 kf = *(const u32x4 *)(klds + (b * KS + ks) * 1024 + lane * 16);
+#pragma unroll
+                for (int c = 0; c < NGRP; ++c)
+                    acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, kf), bq[c][ks], acc[b][c], 0, 0, 0);
+            }
+        float sc[NB][4];
         float tmax = -INFINITY;
 #pragma unroll
-        for (int b = 0; b < NBLK; ++b) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int part = 0; part < 3; ++part)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, kreg[b][ks]), bq[part][ks], acc, 0, 0, 0);
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = jt + b * 16 + grp * 4 + i;
-                const float v = key < j1 ? acc[i] * p.scale_log2 : -INFINITY;
+                float v;
+                if (NGRP == 1) {
+                    v = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < NPART; ++q)
+                        v += __shfl(acc[b][0][i], lg * 16 + min(chead + q * GS, 15), 64);
+                } else {
+                    v = acc[b][0][i] + acc[b][1][i];
+                }
+                v = (jt + b * 16 + lg * 4 + i < j1) ? v * p.scale_log2 : -INFINITY;
                 sc[b][i] = v;
                 tmax = fmaxf(tmax, v);
             }
-        }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = exp2f(m_run - m_new);
-        float psum = 0.0f;
+        // the running max moves only when a column max grows past the headroom;
+        // weights stay <= 2^HEADROOM and O is rescaled rarely
+        const bool grow = tmax > m_run + HEADROOM;
+        if (__any(grow)) {
+            const float m_new = grow ? tmax : m_run;
+            const float alpha = exp2_nonpos(m_run - m_new);
+            l_run *= alpha;
 #pragma unroll
-        for (int b = 0; b < NBLK; ++b)
+            for (int c = 0; c < NGRP; ++c)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    O[c][db] *= alpha;
+            m_run = m_new;
+        }
+        float pv[NB][4];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pv = exp2f(sc[b][i] - m_new);
-                psum += pv;
-                if (n < GP)
-                    p_lds[(b * 16 + grp * 4 + i) * GP + n] = pv;
+                pv[b][i] = ccol ? exp2_nonpos(sc[b][i] - m_run) : 0.0f;
+                l_run += pv[b][i];
             }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (grp == 0 && n < GP)
-            alpha_lds[n] = alpha;
-        __syncthreads();
 
-        float al[GP];
+        // PV: k slot j < 4 is key 4 lg + j of block 0, slot 4 + j of block 1
+        bf16x8 pb[NGRP];
 #pragma unroll
-        for (int g = 0; g < GP; ++g)
-            al[g] = alpha_lds[g];
+        for (int c = 0; c < NGRP; ++c) {
+            const int part = NGRP == 1 ? min(cpart, NPART - 1) : c;
+            u32x4 w;
 #pragma unroll
-        for (int g = 0; g < GP; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                o[g][e] *= al[g];
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-            const int kk = st * KPS + kq;
-            float v[8];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                v[2 * w] = bf_lo(vreg[st][w]);
-                v[2 * w + 1] = bf_hi(vreg[st][w]);
+            for (int e = 0; e < 4; ++e) {
+                const int b = e >> 1, i = (e & 1) * 2;
+                w[e] = bf16_part<NPART>(pv[b][i], part) | (bf16_part<NPART>(pv[b][i + 1], part) << 16);
             }
+            pb[c] = __builtin_bit_cast(bf16x8, w);
+        }
 #pragma unroll
-            for (int g = 0; g < GP; ++g) {
-                const float pg = p_lds[kk * GP + g];
+        for (int db = 0; db < NDB; ++db) {
+            const int col = (db * 16 + 4 * (n & 3)) * 2;
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(vlds + (lg * 4 + (n >> 2)) * VROW + col));
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(vlds + (16 + lg * 4 + (n >> 2)) * VROW +
+                                                            col));
+            const s16x4 vv[2] = {v0, v1};
+            const bf16x8 vt = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    o[g][e] += pg * v[e];
-            }
+            for (int c = 0; c < NGRP; ++c)
+                O[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb[c], O[c][db], 0, 0, 0);
         }
         __syncthreads();
+        if (more) {
+            store_tile(jt + TK);
+            __syncthreads();
+        }
     }
 
-    // sum over the four row groups (l) and over the key slots (o)
+    // ---- per-split partial: reference max, sum and unnormalized output per head
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
+    const size_t base = ((size_t)a * p.Hq + (size_t)h * G) * p.NS;
+    const bool writer = n < G;
 #pragma unroll
-    for (int g = 0; g < GP; ++g)
+    for (int db = 0; db < NDB; ++db) {
+        f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v = o[g][e];
+        for (int i = 0; i < 4; ++i) {
+            float v;
+            if (NGRP == 1) {
+                v = 0.0f;
 #pragma unroll
-            for (int off = LPK; off < 64; off <<= 1)
-                v += __shfl_xor(v, off, 64);
-            o[g][e] = v;
-        }
-
-    const size_t base = ((size_t)a * p.Hq + (size_t)h * G) * p.NS + s;
-    if (kq == 0) {
-#pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            if (g < G) {
-                float *dst = p.part_o + (base + (size_t)g * p.NS) * D + dc * 8;
-                *(f32x4 *)dst = f32x4{o[g][0], o[g][1], o[g][2], o[g][3]};
-                *(f32x4 *)(dst + 4) = f32x4{o[g][4], o[g][5], o[g][6], o[g][7]};
+                for (int q = 0; q < NPART; ++q)
+                    v += __shfl(O[0][db][i], lg * 16 + min(n + q * GS, 15), 64);
+            } else {
+                v = O[0][db][i] + O[1][db][i];
             }
+            o[i] = v;
         }
+        if (writer)
+            *(f32x4 *)(p.part_o + (base + (size_t)n * p.NS + s) * D + db * 16 + lg * 4) = o;
     }
-    if (grp == 0 && n < G) {
-        float *dst = p.part_ml + (base + (size_t)n * p.NS) * 2;
+    if (writer && lg == 0) {
+        float *dst = p.part_ml + (base + (size_t)n * p.NS + s) * 2;
         dst[0] = m_run;
         dst[1] = l_run;
     }
 }
 
+
 // ---------------------------------------------------------------- R4
+// One wave per (entry, query head): lanes read the split statistics in
+// parallel, the unnormalized split outputs are summed with weights
+// 2^(m_s - M) (loads issued four splits at a time), divided by the weighted
+// sum of l_s and rounded to BF16.
 template <int D>
 __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
 {
@@ -389,19 +560,44 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
     const float *ml = p.part_ml + base * 2;
     const float *po = p.part_o + base * D;
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s)
-        M = fmaxf(M, ml[2 * s]);
-    float L = 0.0f, O[PER];
+    for (int c = lane; c < ns; c += 64)
+        M = fmaxf(M, ml[2 * c]);
+    M = wave_max(M);
+    float lw = 0.0f, O[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e)
         O[e] = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-        const float w = exp2f(ml[2 * s] - M);
-        L += w * ml[2 * s + 1];
+    for (int c = 0; c < ns; c += 64) {
+        float w = 0.0f;
+        if (c + lane < ns) {
+            w = exp2f(ml[2 * (c + lane)] - M);
+            lw += w * ml[2 * (c + lane) + 1];
+        }
+        const int cnt = min(64, ns - c);
+        int k = 0;
+        for (; k + 4 <= cnt; k += 4) {
+            float wk[4], x[4][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-            O[e] += w * po[(size_t)s * D + lane + 64 * e];
+            for (int u = 0; u < 4; ++u) {
+                wk[u] = __shfl(w, k + u, 64);
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    x[u][e] = po[(size_t)(c + k + u) * D + lane + 64 * e];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    O[e] += wk[u] * x[u][e];
+        }
+        for (; k < cnt; ++k) {
+            const float wk = __shfl(w, k, 64);
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                O[e] += wk * po[(size_t)(c + k) * D + lane + 64 * e];
+        }
     }
+    const float L = wave_sum(lw);
 #pragma unroll
     for (int e = 0; e < PER; ++e)
         out[lane + 64 * e] = (uint16_t)f2bf(O[e] / L);
@@ -409,7 +605,8 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
 
 }  // namespace
 
-DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t D, int64_t NS)
+DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t Hkv, int64_t D,
+                                        int64_t NS)
 {
     auto up = [](uint64_t x) { return (x + 255u) & ~uint64_t(255); };
     DecodeWorkspace w;
@@ -417,6 +614,7 @@ DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t D, int64_
     w.part_o_off = up(w.qrot_off + (uint64_t)A * Hq * D * 4);
     w.part_ml_off = up(w.part_o_off + (uint64_t)A * Hq * NS * D * 4);
     w.total = up(w.part_ml_off + (uint64_t)A * Hq * NS * 2 * 4);
+    (void)Hkv;
     return w;
 }
 
@@ -427,25 +625,28 @@ hipError_t launch_rope_store(const DecodeParams &p, hipStream_t stream)
 }
 
 template <int D>
-static hipError_t launch_split_d(const DecodeParams &p, hipStream_t stream)
+static hipError_t launch_fused_d(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
+                                 hipEvent_t e1)
 {
     const dim3 grid(p.NS, p.Hkv, p.A), block(64);
     if (p.G <= 1)
-        hipLaunchKernelGGL((k_decode_split<D, 1>), grid, block, 0, stream, p);
+        hipExtLaunchKernelGGL((k_decode_fused<D, 1>), grid, block, 0, stream, e0, e1, 0, p);
     else if (p.G <= 2)
-        hipLaunchKernelGGL((k_decode_split<D, 2>), grid, block, 0, stream, p);
+        hipExtLaunchKernelGGL((k_decode_fused<D, 2>), grid, block, 0, stream, e0, e1, 0, p);
     else if (p.G <= 4)
-        hipLaunchKernelGGL((k_decode_split<D, 4>), grid, block, 0, stream, p);
+        hipExtLaunchKernelGGL((k_decode_fused<D, 4>), grid, block, 0, stream, e0, e1, 0, p);
     else if (p.G <= 8)
-        hipLaunchKernelGGL((k_decode_split<D, 8>), grid, block, 0, stream, p);
+        hipExtLaunchKernelGGL((k_decode_fused<D, 8>), grid, block, 0, stream, e0, e1, 0, p);
     else
-        hipLaunchKernelGGL((k_decode_split<D, 16>), grid, block, 0, stream, p);
+        hipExtLaunchKernelGGL((k_decode_fused<D, 16>), grid, block, 0, stream, e0, e1, 0, p);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_split(const DecodeParams &p, hipStream_t stream)
+hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
+                               hipEvent_t e1)
 {
-    return p.D == 64 ? launch_split_d<64>(p, stream) : launch_split_d<128>(p, stream);
+    return p.D == 64 ? launch_fused_d<64>(p, stream, e0, e1)
+                     : launch_fused_d<128>(p, stream, e0, e1);
 }
 
 hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream)
@@ -458,13 +659,14 @@ hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream)
+hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
+                                  hipEvent_t e1)
 {
     const dim3 grid(p.Hq, p.A), block(64);
     if (p.D == 64)
-        hipLaunchKernelGGL(k_decode_readable<64>, grid, block, 0, stream, p);
+        hipExtLaunchKernelGGL(k_decode_readable<64>, grid, block, 0, stream, e0, e1, 0, p);
     else
-        hipLaunchKernelGGL(k_decode_readable<128>, grid, block, 0, stream, p);
+        hipExtLaunchKernelGGL(k_decode_readable<128>, grid, block, 0, stream, e0, e1, 0, p);
     return hipGetLastError();
 }
 

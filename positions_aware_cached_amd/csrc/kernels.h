@@ -36,16 +36,20 @@ struct DecodeParams {
 struct DecodeWorkspace {
     uint64_t qrot_off, part_o_off, part_ml_off, total;
 };
-DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t D, int64_t NS);
+DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t Hkv, int64_t D,
+                                        int64_t NS);
 
 // RoPE(K) + K/V store + RoPE(Q) -> qrot.  One block per active entry.
 hipError_t launch_rope_store(const DecodeParams &p, hipStream_t stream);
-// Tuned split-K attention: per-split partials into the workspace.
-hipError_t launch_decode_split(const DecodeParams &p, hipStream_t stream);
-// Cross-split merge -> BF16 output.
+// Tuned decode step: RoPE + store + split-K attention + merge in one launch.
+// e0 / e1: optional events stamped at the kernel's start and end.
+hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
+                               hipEvent_t e1);
+// Cross-split merge -> BF16 output (one wave per entry and query head).
 hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream);
 // Readable one-wave-per-(entry, query head) attention straight to the output.
-hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
+                                  hipEvent_t e1);
 
 struct PrefillParams {
     const uint16_t *q;      // [A, T, Hq, D]

@@ -68,6 +68,11 @@ mllm_status check_desc(const mllm_cache_desc *d)
         return fail(MLLM_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d->head_dim);
     if (d->device < 0)
         return fail(MLLM_ERR_INVALID_ARG, "device ordinal %d is negative", d->device);
+    if ((uint64_t)d->capacity * d->h_kv * d->head_dim * 2 >= (1ull << 31))
+        return fail(MLLM_ERR_UNSUPPORTED, "one cache row (capacity * h_kv * head_dim * 2 bytes) "
+                    "must stay below 2 GiB");
+    if (d->capacity >= (1 << 24))
+        return fail(MLLM_ERR_UNSUPPORTED, "capacity must be below 2^24");
     return MLLM_OK;
 }
 
@@ -172,6 +177,9 @@ mllm_status resolve_opts(const mllm_decode_opts *opts, int *kps, int *kernel)
     *kernel = 0;
     if (!opts)
         return MLLM_OK;
+    for (int i = 0; i < 4; ++i)
+        if (opts->reserved[i] != 0)
+            return fail(MLLM_ERR_INVALID_ARG, "reserved option fields must be zero");
     if (opts->keys_per_split != 0) {
         if (opts->keys_per_split < 64 || opts->keys_per_split > 65536 ||
             opts->keys_per_split % 64 != 0)
@@ -371,7 +379,7 @@ mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32
         return st;
     const int maxp = max_position < 0 ? d.capacity - 1 : max_position;
     const int ns = splits_for(maxp, kps);
-    *bytes = mllm::decode_workspace_layout(A, h_q, d.head_dim, ns).total;
+    *bytes = mllm::decode_workspace_layout(A, h_q, d.h_kv, d.head_dim, ns).total;
     return ok();
 }
 
@@ -445,7 +453,7 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
         }
     }
     const int ns = splits_for(maxp, kps);
-    const mllm::DecodeWorkspace wl = mllm::decode_workspace_layout(A, Hq, D, ns);
+    const mllm::DecodeWorkspace wl = mllm::decode_workspace_layout(A, Hq, d.h_kv, D, ns);
     if (A > 0) {
         if (!workspace)
             return fail(MLLM_ERR_WORKSPACE, "workspace is null");
@@ -509,21 +517,21 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     fill_inv_freq(p.inv_freq, rope->base, D);
 
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = mllm::launch_rope_store(p, s);
-    if (e != hipSuccess)
-        return hip_fail(e, "rope/store launch");
-    if (kernel == 1) {
-        e = mllm::launch_decode_readable(p, s);
+    hipEvent_t *ev = opts ? (hipEvent_t *)opts->attn_events : nullptr;
+    hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+    hipError_t e;
+    if (kernel == 1) {  // readable path: a store kernel, then one wave per query head
+        e = mllm::launch_rope_store(p, s);
         if (e != hipSuccess)
-            return hip_fail(e, "readable attention launch");
+            return hip_fail(e, "rope/store launch");
+        e = mllm::launch_decode_readable(p, s, e0, e1);
     } else {
-        e = mllm::launch_decode_split(p, s);
-        if (e != hipSuccess)
-            return hip_fail(e, "split attention launch");
-        e = mllm::launch_decode_merge(p, s);
-        if (e != hipSuccess)
-            return hip_fail(e, "merge launch");
+        e = mllm::launch_decode_fused(p, s, e0, e1);
+        if (e == hipSuccess)
+            e = mllm::launch_decode_merge(p, s);
     }
+    if (e != hipSuccess)
+        return hip_fail(e, "attention launch");
     if (host_mirror) {
         for (int a = 0; a < A; ++a) {
             const int32_t r = host_mirror[A + a], pos = host_mirror[a];

@@ -121,6 +121,31 @@ def draw_decode(cfg, device="cpu"):
     return dict(q=q, k_new=k_new, v_new=v_new, Kc=Kc, Vc=Vc, positions=pos, rows=rows)
 
 
+def draw_cache_layers(cfg, layers, device="cuda"):
+    """Extra layer caches (K, V pairs) for a decode config, each [S, C, Hkv, D]
+    N(0, sigma) BF16, seeded per layer; inactive rows get the sentinel if the
+    config says so.  Used to rotate layers so a step does not re-read bytes a
+    previous step left in the last-level cache."""
+    S, C, Hkv, D = (cfg[k] for k in ("S", "C", "Hkv", "D"))
+    sigma = cfg.get("sigma", 1.0)
+    _, rows = draw_indices(cfg)
+    out = []
+    for l in range(layers):
+        gen = torch.Generator(device=device)
+        gen.manual_seed(5000 + 97 * cfg["seed"] + l)
+        Kc = _normal_bf16((S, C, Hkv, D), gen, device, sigma)
+        Vc = _normal_bf16((S, C, Hkv, D), gen, device, sigma)
+        if cfg.get("inactive") == "sentinel":
+            inactive = np.setdiff1d(np.arange(S), rows)
+            if inactive.size:
+                idx = torch.as_tensor(inactive, device=device, dtype=torch.long)
+                sent = torch.tensor(NAN_SENTINEL, dtype=torch.int16).view(torch.bfloat16).item()
+                Kc.index_fill_(0, idx, sent)
+                Vc.index_fill_(0, idx, sent)
+        out.append((Kc, Vc))
+    return out
+
+
 def draw_prefill(cfg, device="cpu"):
     """Inputs of one equal-length prefill: q [A,T,Hq,D], k_new/v_new [A,T,Hkv,D],
     Kc/Vc [S,C,Hkv,D] with random prior bytes (the rows are logically empty),
