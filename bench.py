@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak, published
 METRIC = "decode attn step: KV GB/s and % of HBM peak; tokens/s at A rows, ctx"
 
 
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--kernel", type=int, default=0, help="0 tuned split-K, 1 readable")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--prefill-steps", type=int, default=20,
+                    help="also time the equal-length batched prefill (0 = skip)")
     return ap.parse_args()
 
 
@@ -194,11 +197,78 @@ def main():
         },
     }
 
+    if args.prefill_steps > 0:
+        res["prefill"] = bench_prefill(args, hip)
     if args.cpu_seconds > 0:
         call(0)  # a fresh layer-0 step: the oracle sample is compared with it
         torch.cuda.synchronize()
         res["cpu_baseline"] = cpu_baseline(args, cfg, inp, layers[0], pos_h, rows_h, out)
     print(json.dumps(res), flush=True)
+
+
+def bench_prefill(args, hip):
+    """Equal-length batched prefill (16 prompts x 1024 tokens, 32/8/128): the
+    attention kernel's own duration from events stamped in its dispatch; the
+    store kernel runs before it in every step."""
+    import torch
+
+    import positions_aware_cached_amd as pac
+    import workloads
+
+    cfg = workloads.config("prefill")
+    A, T, Hq, Hkv, D = (cfg[k] for k in ("A", "T", "Hq", "Hkv", "D"))
+    inp = workloads.draw_prefill(cfg, device="cuda")
+    cache = pac.Cache.wrap([inp["Kc"]], [inp["Vc"]])
+    rows_h = inp["rows"]
+    rows = torch.as_tensor(rows_h, device="cuda")
+    out = torch.empty_like(inp["q"])
+    ws = torch.empty(max(256, pac.prefill_workspace_size(cache, A, T, Hq)), dtype=torch.uint8,
+                     device="cuda")
+    K = args.prefill_steps
+    evs = []
+    for _ in range(K):
+        pair = (ctypes.c_void_p * 2)()
+        for j in range(2):
+            h = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(h)) == 0
+            pair[j] = h.value
+        evs.append(pair)
+
+    def step(ev=None):
+        for r in rows_h:
+            cache.reset_row(int(r))
+        pac.prefill_rope_store_attn(cache, 0, inp["q"], inp["k_new"], inp["v_new"], rows, rows_h,
+                                    out, ws, cfg["base"], attn_events=ev)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / K
+    ms = []
+    for pair in evs:
+        f = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(pair[0]),
+                                       ctypes.c_void_p(pair[1])) == 0
+        ms.append(f.value)
+        hip.hipEventDestroy(ctypes.c_void_p(pair[0]))
+        hip.hipEventDestroy(ctypes.c_void_p(pair[1]))
+    attn_ms = float(np.mean(ms))
+    flops = 4.0 * D * Hq * A * T * (T + 1) / 2.0            # causal QK^T and PV
+    hbm = (A * T * Hq * D * 2 * 2                            # q read, out written
+           + 2 * A * T * Hkv * D * 2 * 2)                    # k/v read, K/V stored
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    return {"workload": "prefill_16x1024", "A": A, "T": T, "h_q": Hq, "h_kv": Hkv, "head_dim": D,
+            "ms_per_step": round(wall * 1e3, 4), "attn_kernel_ms": round(attn_ms, 4),
+            "causal_gflop": round(flops / 1e9, 2),
+            "roofline": {"kernel": "k_prefill_mfma", "bound": "mfma",
+                         "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None},
+            "hbm_gbs_step": round(hbm / wall / 1e9, 1)}
 
 
 def cpu_baseline(args, cfg, inp, layer0, pos_h, rows_h, out_gpu):

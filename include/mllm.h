@@ -91,7 +91,7 @@ typedef struct {
     int32_t reserved;
 } mllm_rope_desc;
 
-/* Optional knobs of the decode call (NULL = defaults). */
+/* Optional knobs of the decode and prefill calls (NULL = defaults). */
 typedef struct {
     int32_t keys_per_split; /* 0 = default; else a multiple of 64 in [64, 65536] */
     int32_t kernel;         /* 0 = tuned split-K kernel, 1 = readable one-wave-per-head kernel */
@@ -221,6 +221,8 @@ mllm_status mllm_prefill_workspace_size(const mllm_cache *cache, int32_t A, int3
  *                    same values (required: rows are checked in range,
  *                    distinct and logically empty, else MLLM_ERR_ROW_BUSY).
  *  1 <= T <= capacity.  On success every target row's length becomes T.
+ *  opts (may be NULL): kernel 0 = matrix-core kernel, 1 = readable kernel;
+ *  attn_events timestamps the attention kernel; keys_per_split is ignored.
  *  Other arguments as for the decode call.
  */
 mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
@@ -231,7 +233,8 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
                                          const int32_t *cache_rows_host, int32_t A, int32_t T,
                                          const mllm_rope_desc *rope,
                                          const mllm_tensor_view *out, void *workspace,
-                                         uint64_t workspace_bytes, void *stream);
+                                         uint64_t workspace_bytes, const mllm_decode_opts *opts,
+                                         void *stream);
 
 #ifdef __cplusplus
 }

@@ -90,7 +90,7 @@ def load(path=LIB_PATH):
     L.mllm_prefill_workspace_size.argtypes = [vp, i32, i32, i32, P(u64)]
     L.mllm_prefill_rope_store_attn.argtypes = [
         vp, i32, P(TensorView), P(TensorView), P(TensorView), vp, P(i32), i32, i32,
-        P(RopeDesc), P(TensorView), vp, u64, vp]
+        P(RopeDesc), P(TensorView), vp, u64, P(DecodeOpts), vp]
     _lib = L
     return L
 
@@ -251,10 +251,14 @@ def prefill_workspace_size(cache, A, T, h_q):
 
 
 def prefill_rope_store_attn(cache, layer, q, k_new, v_new, rows_dev, rows_host, out, workspace,
-                            base, stream=None):
-    """Equal-length prefill of one layer (see mllm_prefill_rope_store_attn)."""
+                            base, kernel=0, attn_events=None, stream=None):
+    """Equal-length prefill of one layer (see mllm_prefill_rope_store_attn).
+
+    kernel: 0 matrix-core kernel, 1 readable kernel.
+    """
     A, T = q.shape[0], q.shape[1]
     rope = RopeDesc(float(base), q.shape[-1], 0)
+    o = _opts(0, kernel, attn_events)
     rh = torch.as_tensor(rows_host, dtype=torch.int32).contiguous()
     _check(load().mllm_prefill_rope_store_attn(
         cache.handle, layer, ctypes.byref(view(q)), ctypes.byref(view(k_new)),
@@ -262,7 +266,7 @@ def prefill_rope_store_attn(cache, layer, q, k_new, v_new, rows_dev, rows_host, 
         ctypes.cast(rh.data_ptr(), ctypes.POINTER(ctypes.c_int32)), A, T, ctypes.byref(rope),
         ctypes.byref(view(out)), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
-        _stream(stream)))
+        ctypes.byref(o), _stream(stream)))
 
 
 class DecodeCall:

@@ -51,11 +51,15 @@ __device__ __forceinline__ uint32_t f2bf(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Split-half rotation of one pair, every product and sum rounded separately.
+// Split-half rotation of one pair, every product and sum rounded separately
+// (contraction into fused multiply-adds is switched off: the BF16 rounding of
+// the result must see the same FP32 value as a separately rounded evaluation).
 __device__ __forceinline__ void rope_pair(float x, float y, float c, float s, float &lo, float &hi)
 {
-    lo = __fsub_rn(__fmul_rn(x, c), __fmul_rn(y, s));
-    hi = __fadd_rn(__fmul_rn(y, c), __fmul_rn(x, s));
+#pragma clang fp contract(off)
+    const float xc = x * c, ys = y * s, yc = y * c, xs = x * s;
+    lo = xc - ys;
+    hi = yc + xs;
 }
 
 __device__ __forceinline__ bool entry_valid(const DecodeParams &p, int pos, int row)

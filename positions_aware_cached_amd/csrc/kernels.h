@@ -60,12 +60,15 @@ struct PrefillParams {
     uint16_t *kc, *vc;      // layer blocks [S, C, Hkv, D]
     uint16_t *out;          // [A, T, Hq, D]
     int64_t o_sa, o_st, o_sh;
-    uint16_t *qrot;         // workspace [A, Hq, T, D] bf16 rotated queries (head-major)
+    float2 *table;          // workspace [T, D/2] (cos, sin) of positions 0 .. T-1
     int32_t A, T, S, C, Hq, Hkv, D, G;
     float scale_log2;
     float inv_freq[kMaxHalfDim];
 };
 uint64_t prefill_workspace_bytes(int64_t A, int64_t T, int64_t Hq, int64_t D);
-hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
+// RoPE(K) + K/V store, then attention: kernel 0 = matrix-core tiles, 1 = readable.
+// e0 / e1: optional events stamped at the attention kernel's start and end.
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream, int kernel, hipEvent_t e0,
+                          hipEvent_t e1);
 
 }  // namespace mllm

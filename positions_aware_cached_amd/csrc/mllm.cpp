@@ -565,7 +565,8 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
                                          const int32_t *cache_rows_host, int32_t A, int32_t T,
                                          const mllm_rope_desc *rope,
                                          const mllm_tensor_view *out, void *workspace,
-                                         uint64_t workspace_bytes, void *stream)
+                                         uint64_t workspace_bytes, const mllm_decode_opts *opts,
+                                         void *stream)
 {
     if (!cache)
         return fail(MLLM_ERR_INVALID_ARG, "cache is null");
@@ -589,6 +590,9 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
     const int G = (int)(Hq / d.h_kv);
     mllm_status st = check_rope(rope, D);
     if (st)
+        return st;
+    int kps_unused, kernel;
+    if ((st = resolve_opts(opts, &kps_unused, &kernel)))
         return st;
     Range rq, rk, rv, ro;
     const int64_t sq[4] = {A, T, Hq, D}, skv[4] = {A, T, d.h_kv, D};
@@ -658,7 +662,7 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
     p.o_sa = out->stride[0];
     p.o_st = out->stride[1];
     p.o_sh = out->stride[2];
-    p.qrot = (uint16_t *)workspace;
+    p.table = (float2 *)workspace;
     p.A = A;
     p.T = T;
     p.S = d.slots;
@@ -669,7 +673,9 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
     p.G = G;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     fill_inv_freq(p.inv_freq, rope->base, D);
-    hipError_t e = mllm::launch_prefill(p, (hipStream_t)stream);
+    hipEvent_t *ev = opts ? (hipEvent_t *)opts->attn_events : nullptr;
+    hipError_t e = mllm::launch_prefill(p, (hipStream_t)stream, kernel, ev ? ev[0] : nullptr,
+                                        ev ? ev[1] : nullptr);
     if (e != hipSuccess)
         return hip_fail(e, "prefill launch");
     for (int a = 0; a < A; ++a)

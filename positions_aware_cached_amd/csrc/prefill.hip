@@ -9,8 +9,14 @@
 //   k_prefill_store     one block per (token t, entry a): split-half RoPE of
 //                       k_new -> BF16 store, v_new bit copy; blocks of entry 0
 //                       also write the FP32 cos/sin table row of position t.
+//   k_prefill_mfma      the tuned attention: one workgroup of four waves per
+//                       (entry, query head, 128-query tile), FlashAttention-
+//                       style online softmax over 64-key tiles on the matrix
+//                       cores (see below).
 //   k_prefill_readable  one wave per (entry, token, query head), keys one at a
-//                       time, FP32 throughout (reference-level kernel).
+//                       time, FP32 throughout (reference-level kernel, kept for
+//                       diagnosis).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -19,6 +25,10 @@ namespace mllm {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -30,10 +40,15 @@ __device__ __forceinline__ uint32_t f2bf(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Split-half rotation of one pair, every product and sum rounded separately
+// (contraction into fused multiply-adds is switched off: the BF16 rounding of
+// the result must see the same FP32 value as a separately rounded evaluation).
 __device__ __forceinline__ void rope_pair(float x, float y, float c, float s, float &lo, float &hi)
 {
-    lo = __fsub_rn(__fmul_rn(x, c), __fmul_rn(y, s));
-    hi = __fadd_rn(__fmul_rn(y, c), __fmul_rn(x, s));
+#pragma clang fp contract(off)
+    const float xc = x * c, ys = y * s, yc = y * c, xs = x * s;
+    lo = xc - ys;
+    hi = yc + xs;
 }
 
 // workspace: cos/sin table [T][D/2] of float2 (cos, sin)
@@ -135,6 +150,221 @@ __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const 
         out[lane + 64 * e] = (uint16_t)f2bf(o[e] / l);
 }
 
+
+// ---------------------------------------------------------------- tuned
+//
+// One workgroup (4 waves, wave w owns queries q0 + 32 w .. + 31) per (entry a,
+// query head hq, query tile q0 .. q0 + 127); the kv head is hq / G.  Key tiles
+// of 64 are staged through two padded LDS buffers (the next tile is loaded
+// into registers while the current one is computed).  Per tile and wave:
+//   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims of K, B =
+//       16 dims x 32 queries of the rotated query): lane l owns query l % 32
+//       and keys 8 (i / 4) + 4 (l / 32) + i % 4 (i < 16) of each 32-key block,
+//       so the softmax over keys is in-lane plus one exchange with lane l ^ 32;
+//   online softmax in FP32 (log2 domain, causal mask on the diagonal);
+//   O^T += V^T P^T on the same instruction: the score registers are already
+//       the B operand (16 keys per k-step, in the key order above) and V^T is
+//       read from the row-major LDS tile with ds_read_b64_tr_b16 in that order.
+// The rotated query and the weights enter the matrix cores as BF16 (rounded
+// to nearest even); products accumulate in FP32; the output is rounded once.
+template <int D>
+__global__ __launch_bounds__(256) void k_prefill_mfma(PrefillParams p, const float2 *table)
+{
+    constexpr int BM = 128, BN = 64;
+    constexpr int KS = D / 16;              // QK k-steps
+    constexpr int NDB = D / 32;             // PV dim blocks
+    constexpr int ROW = D * 2 + 16;         // padded LDS row, bytes
+    constexpr int CPR = D / 8;              // 16-B chunks per key row
+    constexpr int KPL = 256 / CPR;          // key rows per workgroup load instruction
+    constexpr int LPT = BN / KPL;           // loads per thread per tile and tensor
+    constexpr float HEADROOM = 8.0f;
+
+    const int nqt = (p.T + BM - 1) / BM;
+    const int qt = nqt - 1 - (int)blockIdx.x;  // longest causal rows first
+    const int hq = blockIdx.y, a = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int qi = lane & 31, hh = lane >> 5;
+    const int q0 = qt * BM, qw = q0 + w * 32, qrow = qw + qi;
+    const int row = p.rows[a];
+    if (row < 0 || row >= p.S) {  // device rows disagree with the checked host copy
+        if (qrow < p.T && hh == 0)
+            for (int d = 0; d < D; ++d)
+                p.out[a * p.o_sa + qrow * p.o_st + hq * p.o_sh + d] = 0x7fc0;
+        return;
+    }
+    const int kv = hq / p.G;
+    const int nkeys = min(q0 + BM, p.T);
+    const int ntiles = (nkeys + BN - 1) / BN;
+
+    __shared__ __attribute__((aligned(16))) unsigned char klds[2][BN * ROW];
+    __shared__ __attribute__((aligned(16))) unsigned char vlds[2][BN * ROW];
+
+    const size_t slot = (size_t)p.Hkv * D;
+    const size_t rb = (size_t)row * p.C * slot + (size_t)kv * D;
+    const unsigned char *kb = (const unsigned char *)(p.kc + rb);
+    const unsigned char *vb = (const unsigned char *)(p.vc + rb);
+    const uint32_t slotb = (uint32_t)(slot * 2);
+
+    u32x4 kn[LPT], vn[LPT];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const uint32_t off = (uint32_t)min(t * BN + i * KPL + tid / CPR, nkeys - 1) * slotb +
+                                 (tid % CPR) * 16;
+            kn[i] = *(const u32x4 *)(kb + off);
+            vn[i] = *(const u32x4 *)(vb + off);
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int o = (i * KPL + tid / CPR) * ROW + (tid % CPR) * 16;
+            *(u32x4 *)(klds[buf] + o) = kn[i];
+            *(u32x4 *)(vlds[buf] + o) = vn[i];
+        }
+    };
+    load_tile(0);
+
+    // B operands of QK: the rotated query of this lane's row, dims 16 ks + 8 hh + j
+    bf16x8 bq[KS];
+    {
+        const int tq = min(qrow, p.T - 1);
+        const uint16_t *qs = p.q + a * p.q_sa + tq * p.q_st + hq * p.q_sh;
+        float x[KS][8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 v = *(const u32x4 *)(qs + ks * 16 + hh * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[ks][2 * e] = __uint_as_float(v[e] << 16);
+                x[ks][2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+            }
+        }
+        const float2 *cs = table + (size_t)tq * (D / 2);
+#pragma unroll
+        for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float2 c = cs[ks * 16 + hh * 8 + j];
+                float lo, hi;
+                rope_pair(x[ks][j], x[ks + KS / 2][j], c.x, c.y, lo, hi);
+                x[ks][j] = lo;
+                x[ks + KS / 2][j] = hi;
+            }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = f2bf(x[ks][2 * e]) | (f2bf(x[ks][2 * e + 1]) << 16);
+            bq[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    f32x16 O[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            O[db][i] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    store_tile(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const bool more = t + 1 < ntiles;
+        if (more)
+            load_tile(t + 1);
+        const int k0 = t * BN;
+        if (k0 <= qw + 31) {  // some key of the tile is visible to this wave's queries
+            const unsigned char *kt = klds[buf], *vt = vlds[buf];
+            f32x16 st[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    st[b][i] = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x4 kf = *(const u32x4 *)(kt + (b * 32 + qi) * ROW + (ks * 16 + hh * 8) * 2);
+                    st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                                    bq[ks], st[b], 0, 0, 0);
+                }
+            }
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + b * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+                    const float v = key <= qrow ? st[b][i] * p.scale_log2 : -INFINITY;
+                    st[b][i] = v;
+                    tmax = fmaxf(tmax, v);
+                }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const bool grow = tmax > m_run + HEADROOM;
+            if (__any(grow)) {
+                const float m_new = grow ? tmax : m_run;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    O[db] *= alpha;
+                m_run = m_new;
+            }
+            bf16x8 pb[4];
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                u32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(st[k2 >> 1][8 * (k2 & 1) + 2 * e] - m_run);
+                    const float p1 = __builtin_amdgcn_exp2f(st[k2 >> 1][8 * (k2 & 1) + 2 * e + 1] - m_run);
+                    l_run += p0 + p1;
+                    v[e] = f2bf(p0) | (f2bf(p1) << 16);
+                }
+                pb[k2] = __builtin_bit_cast(bf16x8, v);
+            }
+            // PV: slot j of k-step k2 is key 32 (k2 / 2) + 16 (k2 % 2) + 8 (j / 4) + 4 hh + j % 4
+            const int j16 = lane & 15, g = lane >> 4;
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                const int kbase = 32 * (k2 >> 1) + 16 * (k2 & 1) + 4 * hh + (j16 >> 2);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int col = (32 * db + 16 * (g & 1) + 4 * (j16 & 3)) * 2;
+                    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(vt + kbase * ROW + col));
+                    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(vt + (kbase + 8) * ROW + col));
+                    const s16x4 vv[2] = {v0, v1};
+                    O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                                    pb[k2], O[db], 0, 0, 0);
+                }
+            }
+        }
+        if (more)
+            store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    l_run += __shfl_xor(l_run, 32, 64);
+    if (qrow < p.T) {
+        const float inv = 1.0f / l_run;
+        uint16_t *out = p.out + a * p.o_sa + qrow * p.o_st + hq * p.o_sh;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                u32x2 v;
+                v[0] = f2bf(O[db][4 * r] * inv) | (f2bf(O[db][4 * r + 1] * inv) << 16);
+                v[1] = f2bf(O[db][4 * r + 2] * inv) | (f2bf(O[db][4 * r + 3] * inv) << 16);
+                *(u32x2 *)(out + 32 * db + 8 * r + 4 * hh) = v;
+            }
+    }
+}
+
 }  // namespace
 
 uint64_t prefill_workspace_bytes(int64_t A, int64_t T, int64_t Hq, int64_t D)
@@ -144,18 +374,31 @@ uint64_t prefill_workspace_bytes(int64_t A, int64_t T, int64_t Hq, int64_t D)
     return ((uint64_t)T * (D / 2) * 8u + 255u) & ~uint64_t(255);
 }
 
-hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream)
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream, int kernel, hipEvent_t e0,
+                          hipEvent_t e1)
 {
-    float2 *table = (float2 *)p.qrot;
+    float2 *table = p.table;
     hipLaunchKernelGGL(k_prefill_store, dim3(p.T, p.A), dim3(256), 0, stream, p, table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const dim3 grid(p.Hq, p.T, p.A);
-    if (p.D == 64)
-        hipLaunchKernelGGL(k_prefill_readable<64>, grid, dim3(64), 0, stream, p, table);
-    else
-        hipLaunchKernelGGL(k_prefill_readable<128>, grid, dim3(64), 0, stream, p, table);
+    if (kernel == 1) {
+        const dim3 grid(p.Hq, p.T, p.A);
+        if (p.D == 64)
+            hipExtLaunchKernelGGL(k_prefill_readable<64>, grid, dim3(64), 0, stream, e0, e1, 0, p,
+                                  (const float2 *)table);
+        else
+            hipExtLaunchKernelGGL(k_prefill_readable<128>, grid, dim3(64), 0, stream, e0, e1, 0, p,
+                                  (const float2 *)table);
+    } else {
+        const dim3 grid((p.T + 127) / 128, p.Hq, p.A);
+        if (p.D == 64)
+            hipExtLaunchKernelGGL(k_prefill_mfma<64>, grid, dim3(256), 0, stream, e0, e1, 0, p,
+                                  (const float2 *)table);
+        else
+            hipExtLaunchKernelGGL(k_prefill_mfma<128>, grid, dim3(256), 0, stream, e0, e1, 0, p,
+                                  (const float2 *)table);
+    }
     return hipGetLastError();
 }
 

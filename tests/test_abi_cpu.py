@@ -226,7 +226,7 @@ def call_prefill(fc, A=2, T=16, Hq=4, rows_host=(0, 1), ws=FAKE + 0x40000000, ws
     return pac.load().mllm_prefill_rope_store_attn(
         fc.cache.handle, 0, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
         ctypes.c_void_p(FAKE + 0x20000), rh, A, T, ctypes.byref(rope), ctypes.byref(out),
-        ctypes.c_void_p(ws), ws_bytes, None)
+        ctypes.c_void_p(ws), ws_bytes, None, None)
 
 
 def test_prefill_rejections_before_device():
