@@ -44,6 +44,9 @@ def parse():
                     help="budget of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="also time the equal-length batched prefill (0 = skip)")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="only run a plain 1 GiB device copy (5 times): the reference that "
+                         "scales the HBM byte counters of a profiler run")
     return ap.parse_args()
 
 
@@ -67,8 +70,52 @@ def percentile(xs, q):
     return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "positions_aware_cached_amd", "csrc", f)
+                  for f in ("decode.hip", "prefill.hip", "kernels.h")]
+
+
+def source_digest():
+    """Digest of the kernel sources; counter summaries are valid for one digest."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed profiler summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by the same counter on a plain copy of known size),
+    or None when the summary is missing or was taken on other kernel sources."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_digest") != source_digest():
+        return None
+    e = c.get("kernels", {}).get(f"{kernel}@{workload}")
+    return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+def copy_reference():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes": n, "copies": 5}), flush=True)
+
+
 def main():
     args = parse()
+    if args.copy_reference:
+        copy_reference()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the decode path runs on one GPU, rows shard across GPUs with no exchange)",
@@ -191,7 +238,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("k_decode_fused" if args.kernel == 0 else
+                                        "k_decode_readable", f"{args.workload}_decode"),
             "avg_launch_ms": round(attn_avg, 5),
             "algorithmic_bytes_per_launch": kv_bytes,
         },
@@ -267,7 +315,7 @@ def bench_prefill(args, hip):
             "roofline": {"kernel": "k_prefill_mfma", "bound": "mfma",
                          "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None},
+                         "traffic": measured_traffic("k_prefill_mfma", "prefill_16x1024")},
             "hbm_gbs_step": round(hbm / wall / 1e9, 1)}
 
 
