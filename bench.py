@@ -2,8 +2,9 @@
 """Decode-step throughput of the positions-aware cached decode path on one MI355X.
 
 One step = one layer of the whole hot path on one batch of synthetic input:
-RoPE(K) + K/V store into the shared slot cache, RoPE(Q), split-K causal GQA
-attention over every row's prefix, cross-split merge to the BF16 output.
+RoPE(K) + K/V store into the shared slot cache, RoPE(Q), causal GQA attention
+over every row's prefix with the keys of all rows shared evenly by the resident
+waves, then the cross-wave merge to the BF16 output.
 Steps rotate over several layer caches (as a multi-layer decode does), so a
 step never finds its K/V bytes left in the 256 MB last-level cache by the
 previous step.
@@ -38,8 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "ragged", "long"])
     ap.add_argument("--layers", type=int, default=8, help="layer caches rotated over the steps")
-    ap.add_argument("--keys-per-split", type=int, default=0)
-    ap.add_argument("--kernel", type=int, default=0, help="0 tuned split-K, 1 readable")
+    ap.add_argument("--waves", type=int, default=0,
+                    help="waves sharing the keys (0 = the device's resident waves)")
+    ap.add_argument("--kernel", type=int, default=0, help="0 tuned stream, 1 readable")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--prefill-steps", type=int, default=20,
@@ -143,12 +145,12 @@ def main():
     out = torch.empty((A, Hq, D), dtype=torch.bfloat16, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     mirror = np.concatenate([pos_h, rows_h]).astype(np.int32)
-    nws = pac.decode_workspace_size(cache, A, Hq, int(pos_h.max()), args.keys_per_split,
+    nws = pac.decode_workspace_size(cache, A, Hq, int(pos_h.max()), args.waves,
                                     args.kernel)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     call = pac.DecodeCall(cache, inp["q"], inp["k_new"], inp["v_new"], pos, rows, out, ws,
                           cfg["base"], host_mirror=mirror, status=status,
-                          keys_per_split=args.keys_per_split, kernel=args.kernel)
+                          waves=args.waves, kernel=args.kernel)
 
     # algorithmic bytes of one step
     ctx = pos_h.astype(np.int64) + 1
@@ -222,8 +224,8 @@ def main():
         "config": {"workload": f"{args.workload}_decode", "A": A, "slots": S, "capacity": C,
                    "h_q": Hq, "h_kv": Hkv, "head_dim": D, "rope_base": cfg["base"],
                    "ctx_mean": round(float(ctx.mean()), 1), "ctx_max": int(ctx.max()),
-                   "layers_rotated": L, "keys_per_split": args.keys_per_split or 256,
-                   "kernel": "fused split-k" if args.kernel == 0 else "readable"},
+                   "layers_rotated": L, "waves": args.waves or "resident",
+                   "kernel": "fused stream" if args.kernel == 0 else "readable"},
         "pct_hbm_peak": round(100.0 * tot_gbs / PEAK_HBM_GBS, 2),
         "total_gbs": round(tot_gbs, 1),
         "tokens_per_s": round(A / (ms_per_step * 1e-3), 1),
@@ -232,13 +234,13 @@ def main():
         "kv_bytes_per_step": kv_bytes,
         "total_bytes_per_step": total_bytes,
         "roofline": {
-            "kernel": "k_decode_fused" if args.kernel == 0 else "k_decode_readable",
+            "kernel": "k_decode_stream" if args.kernel == 0 else "k_decode_readable",
             "bound": "hbm",
             "achieved": round(attn_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic("k_decode_fused" if args.kernel == 0 else
+            "traffic": measured_traffic("k_decode_stream" if args.kernel == 0 else
                                         "k_decode_readable", f"{args.workload}_decode"),
             "avg_launch_ms": round(attn_avg, 5),
             "algorithmic_bytes_per_launch": kv_bytes,

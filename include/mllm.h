@@ -93,7 +93,10 @@ typedef struct {
 
 /* Optional knobs of the decode and prefill calls (NULL = defaults). */
 typedef struct {
-    int32_t keys_per_split; /* 0 = default; else a multiple of 64 in [64, 65536] */
+    /* Decode: waves that share the keys of all (entry, kv head) segments, each
+     * taking the same number of 32-key tiles.  0 = the device's resident
+     * waves (one per wave slot); else 1 .. 8192.  Ignored by prefill. */
+    int32_t waves;
     int32_t kernel;         /* 0 = tuned split-K kernel, 1 = readable one-wave-per-head kernel */
     /* NULL, or a hipEvent_t[2] that the call records on its stream right before
      * and right after the attention kernel (the split-K kernel, or the readable
@@ -102,6 +105,8 @@ typedef struct {
     void *attn_events;
     int32_t reserved[4];
 } mllm_decode_opts;
+
+#define MLLM_MAX_WAVES 8192
 
 typedef struct mllm_cache mllm_cache; /* opaque */
 
@@ -147,8 +152,10 @@ mllm_status mllm_cache_reset_row(mllm_cache *cache, int32_t row);
 mllm_status mllm_cache_row_length(const mllm_cache *cache, int32_t row, int32_t *len);
 
 /* Workspace bytes needed by mllm_decode_rope_store_attn for A entries and h_q
- * query heads.  max_position bounds every position of the call (-1 = capacity
- * - 1).  opts may be NULL. */
+ * query heads with the given opts (may be NULL).  max_position bounds every
+ * position of the call (-1 = capacity - 1); this build's size does not depend
+ * on it.  The size is the same for every position, so one workspace serves
+ * every step of a decode loop. */
 mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32_t h_q,
                                        int32_t max_position, const mllm_decode_opts *opts,
                                        uint64_t *bytes);
@@ -172,8 +179,7 @@ mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32
  *  host_mirror     : NULL, or host int32[2*A] = {positions[0..A), rows[0..A)},
  *                    the same values as the device arrays.  With it the call
  *                    also rejects out-of-range positions/rows and duplicate
- *                    rows (MLLM_ERR_OUT_OF_RANGE / MLLM_ERR_INVALID_ARG),
- *                    sizes the split grid from the largest position, and
+ *                    rows (MLLM_ERR_OUT_OF_RANGE / MLLM_ERR_INVALID_ARG) and
  *                    updates the row lengths.  Without it the kernels skip the
  *                    store for an out-of-range entry, write NaN to its output
  *                    and set *status_dev to 1; duplicate rows are then the
@@ -181,8 +187,8 @@ mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32
  *  out             : device view [A, H_q, D]; must not overlap any input,
  *                    the cache or the workspace (MLLM_ERR_ALIAS).
  *  workspace       : device buffer of at least mllm_decode_workspace_size()
- *                    bytes (computed with max_position >= every position, or
- *                    -1), 256-byte aligned, caller-owned, contents ignored.
+ *                    bytes (same A, h_q and opts), 256-byte aligned,
+ *                    caller-owned, contents ignored.
  *  status_dev      : NULL or device int32, set to 1 on a device-side index
  *                    error, never cleared by the library.
  *  stream          : hipStream_t (NULL = the null stream).

@@ -52,8 +52,11 @@ class RopeDesc(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+MAX_WAVES = 8192  # largest wave count a decode launch accepts
+
+
 class DecodeOpts(ctypes.Structure):
-    _fields_ = [("keys_per_split", ctypes.c_int32), ("kernel", ctypes.c_int32),
+    _fields_ = [("waves", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("attn_events", ctypes.c_void_p), ("reserved", ctypes.c_int32 * 4)]
 
 
@@ -134,9 +137,9 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _opts(keys_per_split=0, kernel=0, attn_events=None):
+def _opts(waves=0, kernel=0, attn_events=None):
     o = DecodeOpts()
-    o.keys_per_split = keys_per_split
+    o.waves = waves
     o.kernel = kernel
     if attn_events is not None:
         o.attn_events = ctypes.cast(attn_events, ctypes.c_void_p)
@@ -209,16 +212,16 @@ class Cache:
         return n.value
 
 
-def decode_workspace_size(cache, A, h_q, max_position=-1, keys_per_split=0, kernel=0):
+def decode_workspace_size(cache, A, h_q, max_position=-1, waves=0, kernel=0):
     n = ctypes.c_uint64()
-    o = _opts(keys_per_split, kernel)
+    o = _opts(waves, kernel)
     _check(load().mllm_decode_workspace_size(cache.handle, A, h_q, max_position,
                                              ctypes.byref(o), ctypes.byref(n)))
     return n.value
 
 
 def decode_rope_store_attn(cache, layer, q, k_new, v_new, positions, rows, out, workspace,
-                           base, host_mirror=None, status=None, keys_per_split=0, kernel=0,
+                           base, host_mirror=None, status=None, waves=0, kernel=0,
                            attn_events=None, stream=None):
     """One decode step of one layer (see mllm_decode_rope_store_attn in include/mllm.h).
 
@@ -230,7 +233,7 @@ def decode_rope_store_attn(cache, layer, q, k_new, v_new, positions, rows, out, 
     """
     A = q.shape[0]
     rope = RopeDesc(float(base), q.shape[-1], 0)
-    o = _opts(keys_per_split, kernel, attn_events)
+    o = _opts(waves, kernel, attn_events)
     hm = None
     if host_mirror is not None:
         hm_t = torch.as_tensor(host_mirror, dtype=torch.int32).contiguous()
@@ -277,14 +280,14 @@ class DecodeCall:
     """
 
     def __init__(self, cache, q, k_new, v_new, positions, rows, out, workspace, base,
-                 host_mirror=None, status=None, keys_per_split=0, kernel=0, stream=None):
+                 host_mirror=None, status=None, waves=0, kernel=0, stream=None):
         self.L = load()
         self.cache = cache
         self._keep = (q, k_new, v_new, positions, rows, out, workspace, status)
         self.A = q.shape[0]
         self.vq, self.vk, self.vv, self.vo = view(q), view(k_new), view(v_new), view(out)
         self.rope = RopeDesc(float(base), q.shape[-1], 0)
-        self.opts = _opts(keys_per_split, kernel)
+        self.opts = _opts(waves, kernel)
         self.hm_t = None
         self.hm = None
         if host_mirror is not None:

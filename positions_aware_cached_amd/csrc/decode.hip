@@ -5,15 +5,15 @@
 // store and cached attention; rows not named in cache_rows stay untouched.
 //
 // Tuned path, two launches on one stream:
-//   k_decode_fused    one wave per (entry, kv head, key split): RoPE of the
-//                     queries, RoPE(K) + K/V store by the split that holds the
-//                     new position, scores and P.V on the matrix cores, online
-//                     FP32 softmax, per-split partial (max, sum, unnormalized
-//                     output) into the workspace;
+//   k_decode_stream   NW resident waves split the keys of all (entry, kv head)
+//                     segments evenly: RoPE of the queries, RoPE(K) + K/V store
+//                     by the wave that holds a segment's last tile, scores and
+//                     P.V on the matrix cores, online FP32 softmax, one partial
+//                     (max, sum, unnormalized output) per segment and wave;
 //   k_decode_merge    one wave per (entry, query head): rescales and sums the
-//                     split partials (the streaming-attention merge of the
-//                     IPU refactor log, "Flash vs materialized attention"),
-//                     divides, rounds to BF16.
+//                     partials of its segment (the streaming-attention merge
+//                     of the IPU refactor log, "Flash vs materialized
+//                     attention"), divides, rounds to BF16.
 // Readable path (reference level, kept for diagnosis as the operator workflow
 // asks -- operator-development.md, "Acceptance rule"):
 //   k_rope_store      one block per entry: RoPE(K) + K/V store, rotated
@@ -181,29 +181,44 @@ __device__ __forceinline__ float wave_max(float v)
 
 // ---------------------------------------------------------------- R3
 //
-// k_decode_fused: one wave per (entry a, kv head h, key split s).
+// k_decode_stream: the tuned decode step, one launch of NW resident waves.
 //
-// Prologue: cos/sin of the entry's position (one pair index per lane, in
-// double, rounded once); the wave rotates its G query heads itself.  The wave
-// that owns the split holding position pos also rotates k_new, stores K' and
-// V into (row, pos) and patches its own LDS copy of that key, so the key it
-// attends to is exactly the stored one.
+// Work plan.  The keys of every (entry a, kv head h) segment are cut into
+// tiles of kTile keys; segments follow in entry-major order (seg = a * Hkv +
+// h), so segment (a, h) covers the global tiles [Hkv E(a) + h n(a), + n(a)),
+// where n(a) is entry a's tile count (0 for an entry whose position or row is
+// out of range) and E(a) = n(0) + ... + n(a - 1).  Wave w owns the global
+// tiles [t0(w), t0(w + 1)), t0(w) = floor(w NT / NW): every wave gets the same
+// number of tiles whatever the row lengths, so all finish together.  A wave
+// walks its range across segment boundaries, keeps the next tile in flight
+// across them, and writes one partial (reference max, sum, unnormalized
+// output of each of the G query heads) per segment it touches into slot
+// seg + w -- distinct for distinct (seg, w) because waves visit segments in
+// order -- so at most A Hkv + NW slots.
 //
-// Key tiles of 16: while tile t is computed from LDS, tile t+1 is in flight in
-// registers (K in matrix-core operand order, V in row order, 16 B per lane).
-//   QK  v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims of K, B = 32 dims x
-//       16 columns holding the BF16 parts of the FP32 rotated query heads;
-//       lane l ends with the scores of keys 4*(l/16)+i for column l%16.
-//   softmax per column in FP32 (exp2 on log2(e)/sqrt(D)-scaled scores),
-//       running max / sum across tiles.
-//   PV  v_mfma_f32_16x16x16bf16_1k: A = V^T (16 dims x 16 keys) read with
-//       ds_read_b64_tr_b16 from the row-major LDS tile, B = the BF16 parts of
-//       the FP32 weights in the same columns; FP32 accumulators O^T[d][col].
+// Per segment, on entry: cos/sin of the entry's position (one pair index per
+// lane, in double, rounded once), the G rotated queries as matrix-core B
+// operands, and -- in the wave that holds the segment's last tile -- RoPE of
+// k_new and the store of K' and V at (row, pos), staged in LDS so that the
+// wave attends to exactly the stored bytes.
+//
+// Per 32-key tile: the next tile is in flight in registers (K in operand
+// order, V in row order, 16 B per lane) while this one is computed from LDS:
+//   QK  v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims of K, B = 32 dims x 16
+//       columns holding the BF16 parts of the FP32 rotated query heads; lane l
+//       ends with the scores of keys 4 (l / 16) + i of column l % 16.
+//   softmax per column in FP32 (exp2 of log2(e)/sqrt(D)-scaled scores); the
+//       reference max moves only when a column max grows past a headroom, so
+//       the accumulators are rescaled rarely.
+//   PV  the same instruction with A = V^T read by ds_read_b64_tr_b16 from the
+//       row-major padded LDS tile and B = the BF16 parts of the FP32 weights.
 //
 // Operand columns: part q (hi / mid / lo BF16 part) of head g sits in column
-// q*GS + g (GCLS <= 8, one column group) or column g of group q (GCLS 16).
+// q GS + g (GCLS <= 8, one column group) or column g of group q (GCLS 16).
 // Three parts reproduce an FP32 value exactly (GCLS <= 4); two parts carry
 // it to 2^-16 relative (GCLS 8, 16).
+constexpr int kTile = 32;
+
 template <int GCLS>
 struct Cols {
     static constexpr int GS = GCLS;
@@ -237,17 +252,135 @@ __device__ __forceinline__ uint32_t bf16_part(float x, int part)
     return __float_as_uint(r2) >> 16;
 }
 
+// One 16-B global -> LDS load per active lane: lane l's bytes land at
+// lds_base + 16 l (the LDS base is wave-uniform).
+__device__ __forceinline__ void lds_dma16(const void *g, void *lds_base)
+{
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ long long wave_sum_ll(long long v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o, 64);
+        if (lane >= o)
+            v += t;
+    }
+    return v;
+}
+
+// Tile count of entry x from its position and row: 0 when x >= A or the entry
+// is invalid.  Branch-free, so every lane consumes its loads at this point.
+__device__ __forceinline__ int tiles_of(const DecodeParams &p, int x, int pos, int row)
+{
+    const bool ok = (x < p.A) & (pos >= 0) & (pos < p.C) & (row >= 0) & (row < p.S);
+    return ok ? (pos + kTile) / kTile : 0;
+}
+
+// Entries are read 4 x 64 at a time: lane l of block c0 holds entries
+// c0 + 64 k + l (indices clamped into [0, A), so every load is in bounds and
+// all of them are issued before the first is used).
+struct EntryBlock {
+    int pos[4], row[4], na[4];
+};
+__device__ __forceinline__ void load_block(const DecodeParams &p, int c0, int lane, EntryBlock &b)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int x = min(c0 + 64 * k + lane, p.A - 1);
+        b.pos[k] = p.positions[x];
+        b.row[k] = p.rows[x];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        b.na[k] = tiles_of(p, c0 + 64 * k + lane, b.pos[k], b.row[k]);
+}
+
+// NT = Hkv * sum_a n(a) and Hkv * sum_{x < a} n(x), on every lane.
+__device__ void plan_sums(const DecodeParams &p, int a, int lane, long long &NT, long long &before)
+{
+    long long s = 0, sb = 0;
+    for (int c0 = 0; c0 < p.A; c0 += 256) {
+        EntryBlock b;
+        load_block(p, c0, lane, b);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            s += b.na[k];
+            sb += c0 + 64 * k + lane < a ? b.na[k] : 0;
+        }
+    }
+    NT = wave_sum_ll(s) * p.Hkv;
+    before = wave_sum_ll(sb) * p.Hkv;
+}
+
+// The entry holding global tile t < NT, Hkv * E(entry), and the 64-entry chunk
+// around it (lane l: entry ec + l), on every lane.
+__device__ void plan_locate(const DecodeParams &p, long long t, int lane, int &a_out,
+                            long long &base_out, int &ec, int &e_pos, int &e_row, int &e_na)
+{
+    long long run = 0;
+    for (int c0 = 0; c0 < p.A; c0 += 256) {
+        EntryBlock b;
+        load_block(p, c0, lane, b);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int incl = wave_incl_scan(b.na[k], lane);
+            const long long end = run + (long long)p.Hkv * incl;
+            const unsigned long long hit = __ballot(t < end && b.na[k] > 0);
+            if (hit) {
+                const int l = __ffsll((long long)hit) - 1;
+                a_out = c0 + 64 * k + l;
+                base_out = __shfl(end - (long long)p.Hkv * b.na[k], l, 64);
+                ec = c0 + 64 * k;
+                e_pos = b.pos[k];
+                e_row = b.row[k];
+                e_na = b.na[k];
+                return;
+            }
+            run += (long long)p.Hkv * __shfl(incl, 63, 64);
+        }
+    }
+    a_out = p.A;  // not reached for t < NT
+    base_out = run;
+    ec = 0;
+    e_pos = e_row = e_na = 0;
+}
+
+// Waves of the plan: min(launched, NT); then wave w owns tiles
+// [floor(w NT / NW), floor((w + 1) NT / NW)), never an empty range.
+__device__ __forceinline__ int plan_waves(int launched, long long NT)
+{
+    return (int)min((long long)launched, NT);
+}
+
+// Wave that owns global tile t (inverse of t0(w) = floor(w NT / NW)).
+__device__ __forceinline__ int plan_wave_of(long long t, long long NT, int NW)
+{
+    return (int)(((t + 1) * NW - 1) / NT);
+}
+
 #ifndef MLLM_DECODE_WAVES_PER_SIMD
 #define MLLM_DECODE_WAVES_PER_SIMD 2
 #endif
 template <int D, int GCLS>
-__global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) void k_decode_fused(DecodeParams p)
+__global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) void k_decode_stream(
+    DecodeParams p)
 {
     using CL = Cols<GCLS>;
     constexpr int GS = CL::GS, NPART = CL::NPART, NGRP = CL::NGRP;
     constexpr int KS = D / 32;             // QK k-steps (32 dims each)
     constexpr int NDB = D / 16;            // PV dim blocks (16 dims each)
-    constexpr int TK = 32;                 // keys per tile
+    constexpr int TK = kTile;              // keys per tile
     constexpr int NB = TK / 16;            // 16-key MFMA row blocks per tile
     constexpr int LPK = D / 8;             // lanes per key row (16 B each)
     constexpr int KPI = 64 / LPK;          // key rows per V load instruction
@@ -255,125 +388,95 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
     constexpr int VROW = D * 2 + 16;       // padded LDS row of V, bytes
     constexpr float HEADROOM = 8.0f;       // log2 growth of a column max before O is rescaled
 
-    const int s = blockIdx.x, h = blockIdx.y, a = blockIdx.z;
+    const int w = blockIdx.x;
     const int lane = threadIdx.x, n = lane & 15, lg = lane >> 4;
-    const int pos = p.positions[a], row = p.rows[a];
-    const int G = p.G;
-    if (!entry_valid(p, pos, row)) {
-        if (s == 0 && h == 0 && lane == 0 && p.status)
-            p.status[0] = 1;
+    const int G = p.G, Hkv = p.Hkv;
+    // this lane's RoPE frequency (lanes < D / 2), read once
+    const float my_freq = p.inv_freq[lane & (D / 2 - 1)];
+
+    // the plan uses min(launched waves, NT) waves, so each owns at least one tile
+    long long NT, unused;
+    plan_sums(p, 0, lane, NT, unused);
+    const int NW = plan_waves(p.NS, NT);
+    if (w >= NW)
         return;
-    }
-    const int nkeys = pos + 1;
-    const int j0 = s * p.kps;
-    if (j0 >= nkeys)
-        return;
-    const int j1 = min(nkeys, j0 + p.kps);
+    const long long t0 = (long long)w * NT / NW, t1 = (long long)(w + 1) * NT / NW;
 
     __shared__ float cs[D / 2], sn[D / 2];
     __shared__ __attribute__((aligned(16))) unsigned char klds[TK * D * 2];
     __shared__ __attribute__((aligned(16))) unsigned char vlds[TK * VROW];
     __shared__ __attribute__((aligned(16))) uint16_t newk[D], newv[D];  // the new token
+    __shared__ __attribute__((aligned(16))) uint16_t kraw[D];             // its key, unrotated
+    __shared__ __attribute__((aligned(16))) uint16_t qlds[GCLS * D];      // the segment's queries
 
-    const size_t slot = (size_t)p.Hkv * D;
-    const size_t rbase = (size_t)row * p.C * slot + (size_t)h * D;
-    const unsigned char *kb = (const unsigned char *)(p.kc + rbase);
-    const unsigned char *vb = (const unsigned char *)(p.vc + rbase);
+    const size_t slot = (size_t)Hkv * D;
     const uint32_t slotb = (uint32_t)(slot * 2);  // bytes per position; a row fits in 2^31
+    const int chead = NGRP == 1 ? n % GS : n;     // head of this lane's column
+    const int cpart = NGRP == 1 ? n / GS : 0;     // part of this lane's column (one group)
+    const bool ccol = chead < G && (NGRP == 2 || cpart < NPART);
 
-    // ---- tile staging: registers (in flight) -> LDS (computed)
+    // ---- entry table: lane l holds position, row and tile count of entry ec + l
+    int ec, e_pos, e_row, e_na;
+    int a, h, j, na, row, pos;
+    long long ebase;
+    plan_locate(p, t0, lane, a, ebase, ec, e_pos, e_row, e_na);
+    auto entry = [&](int e, int &pos_o, int &row_o, int &na_o) {
+        if (e < ec || e >= ec + 64) {  // wave-uniform; once per 64 entries
+            ec = e & ~63;
+            const int x = ec + lane, xc = min(x, p.A - 1);
+            e_pos = p.positions[xc];
+            e_row = p.rows[xc];
+            e_na = tiles_of(p, x, e_pos, e_row);
+        }
+        pos_o = __shfl(e_pos, e - ec, 64);
+        row_o = __shfl(e_row, e - ec, 64);
+        na_o = __shfl(e_na, e - ec, 64);
+    };
+    entry(a, pos, row, na);
+    {
+        const long long loc = t0 - ebase;
+        h = (int)(loc / na);
+        j = (int)(loc - (long long)h * na);
+    }
+
+    // ---- the tile in flight (nxt); cur is (a, h, j)
+    int nxa = a, nxh = h, nxj = j, nxna = na, nxrow = row, nxpos = pos;
+    long long nxbase = ebase;
+    auto advance = [&]() {  // nxt := the tile after nxt
+        if (++nxj < nxna)
+            return;
+        nxj = 0;
+        if (++nxh < Hkv)
+            return;
+        nxh = 0;
+        nxbase += (long long)Hkv * nxna;
+        do {
+            ++nxa;
+            entry(nxa, nxpos, nxrow, nxna);
+        } while (nxna == 0 && nxa < p.A);
+    };
+
+    auto seg_base = [&](int srow, int eh, const uint16_t *blk) {
+        return (const unsigned char *)(blk + (size_t)srow * p.C * slot + (size_t)eh * D);
+    };
+
     u32x4 kn[NB][KS], vn[VLD];
-    auto load_tile = [&](int jt) {
+    auto load_tile = [&](const unsigned char *kb, const unsigned char *vb, int jt, int jend) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const uint32_t off = (uint32_t)min(jt + b * 16 + n, j1 - 1) * slotb + lg * 16;
+            const uint32_t off = (uint32_t)min(jt + b * 16 + n, jend - 1) * slotb + lg * 16;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 kn[b][ks] = *(const u32x4 *)(kb + off + ks * 64);
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
-            const uint32_t off = (uint32_t)min(jt + i * KPI + lane / LPK, j1 - 1) * slotb +
+            const uint32_t off = (uint32_t)min(jt + i * KPI + lane / LPK, jend - 1) * slotb +
                                  (lane % LPK) * 16;
             vn[i] = *(const u32x4 *)(vb + off);
         }
     };
-    load_tile(j0);  // first tile in flight during the prologue below
-
-    if (lane < D / 2) {
-        const float theta = __fmul_rn((float)pos, p.inv_freq[lane]);
-        cs[lane] = (float)cos((double)theta);
-        sn[lane] = (float)sin((double)theta);
-    }
-    __syncthreads();
-
-
-    // ---- the new token: rotate k_new, store K' and V (split holding pos only)
-    const bool owner = j1 == nkeys;
-    if (owner) {
-        if (lane < D / 2) {
-            const uint16_t *k = p.k_new + a * p.kn_sa + h * p.kn_sh;
-            float lo, hi;
-            rope_pair(bf2f(k[lane]), bf2f(k[lane + D / 2]), cs[lane], sn[lane], lo, hi);
-            const uint16_t klo = (uint16_t)f2bf(lo), khi = (uint16_t)f2bf(hi);
-            uint16_t *kd = p.kc + rbase + (size_t)pos * slot;
-            kd[lane] = klo;
-            kd[lane + D / 2] = khi;
-            newk[lane] = klo;
-            newk[lane + D / 2] = khi;
-        }
-        if (lane < LPK) {
-            const u32x4 v = *(const u32x4 *)(p.v_new + a * p.vn_sa + h * p.vn_sh + lane * 8);
-            *(u32x4 *)(p.vc + rbase + (size_t)pos * slot + lane * 8) = v;
-            *(u32x4 *)(newv + lane * 8) = v;
-        }
-    }
-
-    // ---- B operands of QK: BF16 parts of the rotated query, by column
-    bf16x8 bq[NGRP][KS];
-    const int chead = NGRP == 1 ? n % GS : n;   // head of this lane's column
-    const int cpart = NGRP == 1 ? n / GS : 0;   // part of this lane's column (one group)
-    const bool ccol = chead < G && (NGRP == 2 || cpart < NPART);
-    {
-        float qv[KS][8];
-        const uint16_t *qs = p.q + a * p.q_sa + (h * G + (ccol ? chead : 0)) * p.q_sh;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 w = *(const u32x4 *)(qs + ks * 32 + lg * 8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                qv[ks][2 * e] = bf_lo(w[e]);
-                qv[ks][2 * e + 1] = bf_hi(w[e]);
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS / 2; ++ks)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int i = ks * 32 + lg * 8 + j;
-                float lo, hi;
-                rope_pair(qv[ks][j], qv[ks + KS / 2][j], cs[i], sn[i], lo, hi);
-                qv[ks][j] = lo;
-                qv[ks + KS / 2][j] = hi;
-            }
-#pragma unroll
-        for (int c = 0; c < NGRP; ++c) {
-            const int part = NGRP == 1 ? min(cpart, NPART - 1) : c;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4 w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t b0 = ccol ? bf16_part<NPART>(qv[ks][2 * e], part) : 0u;
-                    const uint32_t b1 = ccol ? bf16_part<NPART>(qv[ks][2 * e + 1], part) : 0u;
-                    w[e] = b0 | (b1 << 16);
-                }
-                bq[c][ks] = __builtin_bit_cast(bf16x8, w);
-            }
-        }
-    }
-
-    auto store_tile = [&](int jt) {
+    auto store_tile = [&]() {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -382,37 +485,180 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
 #pragma unroll
         for (int i = 0; i < VLD; ++i)
             *(u32x4 *)(vlds + (i * KPI + lane / LPK) * VROW + (lane % LPK) * 16) = vn[i];
-        if (owner && pos >= jt && pos < jt + TK) {
-            // the key just stored: overwrite the stale copy that was loaded
-            const int kk = pos - jt, b = kk >> 4, m = kk & 15;
-            if (lane < LPK) {
-                // 16-B chunk c = lane of the key: K operand slot (ks, lg) = (c / 4, c % 4)
-                *(u32x4 *)(klds + (b * KS + (lane >> 2)) * 1024 + (m + 16 * (lane & 3)) * 16) =
-                    *(const u32x4 *)(newk + lane * 8);
-                *(u32x4 *)(vlds + kk * VROW + lane * 16) = *(const u32x4 *)(newv + lane * 8);
+    };
+    // The segment's last tile, held by its owner: the key just stored replaces
+    // the stale copy that was loaded, and keys past pos (clamped to pos, with
+    // its stale bytes) get zero values, as they carry zero weight and a stale
+    // NaN times zero would be NaN.
+    auto patch_tile = [&](int kk) {
+        const int b = kk >> 4, m = kk & 15;
+        if (lane < LPK) {
+            // 16-B chunk c = lane of the key: K operand slot (ks, lg) = (c / 4, c % 4)
+            *(u32x4 *)(klds + (b * KS + (lane >> 2)) * 1024 + (m + 16 * (lane & 3)) * 16) =
+                *(const u32x4 *)(newk + lane * 8);
+            *(u32x4 *)(vlds + kk * VROW + lane * 16) = *(const u32x4 *)(newv + lane * 8);
+        }
+        for (int idx = lane; idx < (TK - 1 - kk) * LPK; idx += 64)
+            *(u32x4 *)(vlds + (kk + 1 + idx / LPK) * VROW + (idx % LPK) * 16) =
+                u32x4{0u, 0u, 0u, 0u};
+    };
+
+    // ---- segment inputs: the G query heads, the new key and the new value go
+    // straight from memory into LDS (16 B per lane per load), issued before
+    // the segment's first tile and read only after that tile has arrived
+    bool own_pre = false;
+    int cs_entry = -1;  // entry whose cos/sin sit in cs/sn
+    auto fetch_segment = [&](int ea, int eh, long long eb, int ena) {
+        constexpr int QCH = D / 8;  // 16-B chunks per head
+        const uint16_t *qs = p.q + ea * p.q_sa + eh * G * p.q_sh;
+#pragma unroll
+        for (int c0 = 0; c0 < GCLS * QCH; c0 += 64) {
+            const int c = c0 + lane;
+            if (c < G * QCH)
+                lds_dma16(qs + (c / QCH) * p.q_sh + (c % QCH) * 8, qlds + c0 * 8);
+        }
+        own_pre = eb + (long long)eh * ena + ena - 1 < t1;  // holds the last tile
+        if (own_pre && lane < LPK) {
+            lds_dma16(p.k_new + ea * p.kn_sa + eh * p.kn_sh + lane * 8, kraw);
+            lds_dma16(p.v_new + ea * p.vn_sa + eh * p.vn_sh + lane * 8, newv);
+        }
+    };
+    // cos/sin of entry ea's angles (ALU only; the heads of an entry share them)
+    auto angles = [&](int ea, int epos) {
+        if (ea != cs_entry) {
+            cs_entry = ea;
+            if (lane < D / 2) {
+                const float theta = __fmul_rn((float)epos, my_freq);
+                cs[lane] = (float)cos((double)theta);
+                sn[lane] = (float)sin((double)theta);
             }
-            // keys past pos were clamped to pos and hold its stale bytes: they
-            // carry zero weight, so give them zero values (0 * stale NaN = NaN)
-            for (int idx = lane; idx < (TK - 1 - kk) * LPK; idx += 64)
-                *(u32x4 *)(vlds + (kk + 1 + idx / LPK) * VROW + (idx % LPK) * 16) =
-                    u32x4{0u, 0u, 0u, 0u};
         }
     };
 
-    float m_run = -INFINITY, l_run = 0.0f;
+    // ---- per-segment state
+    int nkeys = 0;
+    bool owner = false;
+    bf16x8 bq[NGRP][KS];
+    float m_run, l_run;
     f32x4 O[NGRP][NDB];
+    auto start_segment = [&](int eh, int erow, int epos) {
+        pos = epos;
+        nkeys = epos + 1;
+        owner = own_pre;
+        __syncthreads();  // cs/sn and the segment inputs written by other lanes
+        if (owner) {
+            const size_t at = ((size_t)erow * p.C + epos) * slot + (size_t)eh * D;
+            if (lane < D / 2) {
+                float lo, hi;
+                rope_pair(bf2f(kraw[lane]), bf2f(kraw[lane + D / 2]), cs[lane], sn[lane], lo, hi);
+                const uint16_t klo = (uint16_t)f2bf(lo), khi = (uint16_t)f2bf(hi);
+                p.kc[at + lane] = klo;
+                p.kc[at + lane + D / 2] = khi;
+                newk[lane] = klo;
+                newk[lane + D / 2] = khi;
+            }
+            if (lane < LPK)
+                *(u32x4 *)(p.vc + at + lane * 8) = *(const u32x4 *)(newv + lane * 8);
+        }
+        // B operands of QK: BF16 parts of the rotated query, by column
+        float qv[KS][8];
+        const unsigned char *qrow = (const unsigned char *)qlds + (ccol ? chead : 0) * D * 2;
 #pragma unroll
-    for (int c = 0; c < NGRP; ++c)
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 v = *(const u32x4 *)(qrow + (ks * 32 + lg * 8) * 2);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-            O[c][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int e = 0; e < 4; ++e) {
+                qv[ks][2 * e] = bf_lo(v[e]);
+                qv[ks][2 * e + 1] = bf_hi(v[e]);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int i = ks * 32 + lg * 8 + jj;
+                float lo, hi;
+                rope_pair(qv[ks][jj], qv[ks + KS / 2][jj], cs[i], sn[i], lo, hi);
+                qv[ks][jj] = lo;
+                qv[ks + KS / 2][jj] = hi;
+            }
+#pragma unroll
+        for (int c = 0; c < NGRP; ++c) {
+            const int part = NGRP == 1 ? min(cpart, NPART - 1) : c;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t b0 = ccol ? bf16_part<NPART>(qv[ks][2 * e], part) : 0u;
+                    const uint32_t b1 = ccol ? bf16_part<NPART>(qv[ks][2 * e + 1], part) : 0u;
+                    v[e] = b0 | (b1 << 16);
+                }
+                bq[c][ks] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+        m_run = -INFINITY;
+        l_run = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NGRP; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                O[c][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+    auto end_segment = [&](int ea, int eh) {
+        float l = l_run;
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        const size_t sl = (size_t)(ea * Hkv + eh + w) * G;  // slot seg + w
+        const bool writer = n < G;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v;
+                if (NGRP == 1) {
+                    v = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < NPART; ++q)
+                        v += __shfl(O[0][db][i], lg * 16 + min(n + q * GS, 15), 64);
+                } else {
+                    v = O[0][db][i] + O[1][db][i];
+                }
+                o[i] = v;
+            }
+            if (writer)
+                *(f32x4 *)(p.part_o + (sl + n) * D + db * 16 + lg * 4) = o;
+        }
+        if (writer && lg == 0) {
+            float *dst = p.part_ml + (sl + n) * 2;
+            dst[0] = m_run;
+            dst[1] = l;
+        }
+    };
 
-    store_tile(j0);
+    // ---- first tile
+    fetch_segment(a, h, ebase, na);
+    load_tile(seg_base(row, h, p.kc), seg_base(row, h, p.vc), j * TK, pos + 1);
+    angles(a, pos);
+    store_tile();
+    start_segment(h, row, pos);
+    if (owner && j == na - 1)
+        patch_tile(pos - j * TK);
     __syncthreads();
-    for (int jt = j0; jt < j1; jt += TK) {
-        const bool more = jt + TK < j1;
-        if (more)
-            load_tile(jt + TK);
+
+    for (long long t = t0; t < t1; ++t) {
+        const bool more = t + 1 < t1;
+        if (more) {
+            advance();
+            // a segment starts at tile 0 except the wave's first one
+            if (nxj == 0)
+                fetch_segment(nxa, nxh, nxbase, nxna);
+            load_tile(seg_base(nxrow, nxh, p.kc), seg_base(nxrow, nxh, p.vc), nxj * TK,
+                      nxpos + 1);
+        }
+        const bool seg_ends = !more || nxj == 0;
+        const int jt = j * TK;
 
         // QK: lane (n, lg) gets keys jt + 16 b + 4 lg + i of column n
         f32x4 acc[NB][NGRP];
@@ -446,14 +692,12 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
                 } else {
                     v = acc[b][0][i] + acc[b][1][i];
                 }
-                v = (jt + b * 16 + lg * 4 + i < j1) ? v * p.scale_log2 : -INFINITY;
+                v = (jt + b * 16 + lg * 4 + i < nkeys) ? v * p.scale_log2 : -INFINITY;
                 sc[b][i] = v;
                 tmax = fmaxf(tmax, v);
             }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        // the running max moves only when a column max grows past the headroom;
-        // weights stay <= 2^HEADROOM and O is rescaled rarely
         const bool grow = tmax > m_run + HEADROOM;
         if (__any(grow)) {
             const float m_new = grow ? tmax : m_run;
@@ -475,18 +719,18 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
                 l_run += pv[b][i];
             }
 
-        // PV: k slot j < 4 is key 4 lg + j of block 0, slot 4 + j of block 1
+        // PV: k slot jj < 4 is key 4 lg + jj of block 0, slot 4 + jj of block 1
         bf16x8 pb[NGRP];
 #pragma unroll
         for (int c = 0; c < NGRP; ++c) {
             const int part = NGRP == 1 ? min(cpart, NPART - 1) : c;
-            u32x4 w;
+            u32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int b = e >> 1, i = (e & 1) * 2;
-                w[e] = bf16_part<NPART>(pv[b][i], part) | (bf16_part<NPART>(pv[b][i + 1], part) << 16);
+                v[e] = bf16_part<NPART>(pv[b][i], part) | (bf16_part<NPART>(pv[b][i + 1], part) << 16);
             }
-            pb[c] = __builtin_bit_cast(bf16x8, w);
+            pb[c] = __builtin_bit_cast(bf16x8, v);
         }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -502,50 +746,40 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
             for (int c = 0; c < NGRP; ++c)
                 O[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb[c], O[c][db], 0, 0, 0);
         }
-        __syncthreads();
+        if (more && seg_ends)
+            angles(nxa, nxpos);  // overlaps the loads in flight
+        __syncthreads();         // LDS of tile t fully read
+
+        // the one wait per tile: tile t+1 (and the segment inputs issued
+        // before it) into LDS; then this segment's partial and the next
+        // segment's start, whose stores drain during the next tile
+        if (more)
+            store_tile();
+        if (seg_ends)
+            end_segment(a, h);
         if (more) {
-            store_tile(jt + TK);
+            if (seg_ends)
+                start_segment(nxh, nxrow, nxpos);
+            a = nxa;
+            h = nxh;
+            j = nxj;
+            na = nxna;
+            row = nxrow;
+            ebase = nxbase;
+            if (owner && j == na - 1)
+                patch_tile(pos - j * TK);
             __syncthreads();
         }
     }
-
-    // ---- per-split partial: reference max, sum and unnormalized output per head
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-    const size_t base = ((size_t)a * p.Hq + (size_t)h * G) * p.NS;
-    const bool writer = n < G;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        f32x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float v;
-            if (NGRP == 1) {
-                v = 0.0f;
-#pragma unroll
-                for (int q = 0; q < NPART; ++q)
-                    v += __shfl(O[0][db][i], lg * 16 + min(n + q * GS, 15), 64);
-            } else {
-                v = O[0][db][i] + O[1][db][i];
-            }
-            o[i] = v;
-        }
-        if (writer)
-            *(f32x4 *)(p.part_o + (base + (size_t)n * p.NS + s) * D + db * 16 + lg * 4) = o;
-    }
-    if (writer && lg == 0) {
-        float *dst = p.part_ml + (base + (size_t)n * p.NS + s) * 2;
-        dst[0] = m_run;
-        dst[1] = l_run;
-    }
 }
 
-
 // ---------------------------------------------------------------- R4
-// One wave per (entry, query head): lanes read the split statistics in
-// parallel, the unnormalized split outputs are summed with weights
-// 2^(m_s - M) (loads issued four splits at a time), divided by the weighted
-// sum of l_s and rounded to BF16.
+// One wave per (entry, query head): the partials of segment (a, h = hq / G)
+// sit in slots seg + w for the waves w that touched it (the same plan as the
+// decode kernel); they are summed with weights 2^(m_w - M) (loads issued four
+// at a time), divided by the weighted sum of l_w and rounded to BF16.  An
+// entry with an out-of-range position or row gets a NaN output and sets the
+// status word.
 template <int D>
 __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
 {
@@ -557,25 +791,33 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
 #pragma unroll
         for (int e = 0; e < PER; ++e)
             out[lane + 64 * e] = 0x7fc0;
+        if (hq == 0 && lane == 0 && p.status)
+            p.status[0] = 1;
         return;
     }
-    const int ns = (pos + p.kps) / p.kps;
-    const size_t base = ((size_t)a * p.Hq + hq) * p.NS;
-    const float *ml = p.part_ml + base * 2;
-    const float *po = p.part_o + base * D;
+    const int G = p.G, h = hq / G, g = hq - h * G;
+    long long NT, before;
+    plan_sums(p, a, lane, NT, before);  // NT >= 1: this entry is valid
+    const int NW = plan_waves(p.NS, NT);
+    const int na = (pos + kTile) / kTile;
+    const long long ts = before + (long long)h * na;
+    const int wf = plan_wave_of(ts, NT, NW), wl = plan_wave_of(ts + na - 1, NT, NW);
+    const int ns = wl - wf + 1;
+    const size_t s0 = (size_t)(a * p.Hkv + h + wf);  // slot of wave wf
     float M = -INFINITY;
     for (int c = lane; c < ns; c += 64)
-        M = fmaxf(M, ml[2 * c]);
+        M = fmaxf(M, p.part_ml[((s0 + c) * G + g) * 2]);
     M = wave_max(M);
     float lw = 0.0f, O[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e)
         O[e] = 0.0f;
     for (int c = 0; c < ns; c += 64) {
-        float w = 0.0f;
+        float wgt = 0.0f;
         if (c + lane < ns) {
-            w = exp2f(ml[2 * (c + lane)] - M);
-            lw += w * ml[2 * (c + lane) + 1];
+            const float *ml = p.part_ml + ((s0 + c + lane) * G + g) * 2;
+            wgt = exp2f(ml[0] - M);
+            lw += wgt * ml[1];
         }
         const int cnt = min(64, ns - c);
         int k = 0;
@@ -583,10 +825,10 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
             float wk[4], x[4][PER];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                wk[u] = __shfl(w, k + u, 64);
+                wk[u] = __shfl(wgt, k + u, 64);
 #pragma unroll
                 for (int e = 0; e < PER; ++e)
-                    x[u][e] = po[(size_t)(c + k + u) * D + lane + 64 * e];
+                    x[u][e] = p.part_o[((s0 + c + k + u) * G + g) * D + lane + 64 * e];
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -595,10 +837,10 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
                     O[e] += wk[u] * x[u][e];
         }
         for (; k < cnt; ++k) {
-            const float wk = __shfl(w, k, 64);
+            const float wk = __shfl(wgt, k, 64);
 #pragma unroll
             for (int e = 0; e < PER; ++e)
-                O[e] += wk * po[(size_t)(c + k) * D + lane + 64 * e];
+                O[e] += wk * p.part_o[((s0 + c + k) * G + g) * D + lane + 64 * e];
         }
     }
     const float L = wave_sum(lw);
@@ -615,10 +857,11 @@ DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t Hkv, int6
     auto up = [](uint64_t x) { return (x + 255u) & ~uint64_t(255); };
     DecodeWorkspace w;
     w.qrot_off = 0;
+    // partial slots: at most A * Hkv segments + NS waves, G heads each
+    const uint64_t slots = ((uint64_t)A * Hkv + NS) * (Hq / Hkv);
     w.part_o_off = up(w.qrot_off + (uint64_t)A * Hq * D * 4);
-    w.part_ml_off = up(w.part_o_off + (uint64_t)A * Hq * NS * D * 4);
-    w.total = up(w.part_ml_off + (uint64_t)A * Hq * NS * 2 * 4);
-    (void)Hkv;
+    w.part_ml_off = up(w.part_o_off + slots * D * 4);
+    w.total = up(w.part_ml_off + slots * 2 * 4);
     return w;
 }
 
@@ -629,28 +872,28 @@ hipError_t launch_rope_store(const DecodeParams &p, hipStream_t stream)
 }
 
 template <int D>
-static hipError_t launch_fused_d(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
-                                 hipEvent_t e1)
+static hipError_t launch_stream_d(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
+                                  hipEvent_t e1)
 {
-    const dim3 grid(p.NS, p.Hkv, p.A), block(64);
+    const dim3 grid(p.NS), block(64);
     if (p.G <= 1)
-        hipExtLaunchKernelGGL((k_decode_fused<D, 1>), grid, block, 0, stream, e0, e1, 0, p);
+        hipExtLaunchKernelGGL((k_decode_stream<D, 1>), grid, block, 0, stream, e0, e1, 0, p);
     else if (p.G <= 2)
-        hipExtLaunchKernelGGL((k_decode_fused<D, 2>), grid, block, 0, stream, e0, e1, 0, p);
+        hipExtLaunchKernelGGL((k_decode_stream<D, 2>), grid, block, 0, stream, e0, e1, 0, p);
     else if (p.G <= 4)
-        hipExtLaunchKernelGGL((k_decode_fused<D, 4>), grid, block, 0, stream, e0, e1, 0, p);
+        hipExtLaunchKernelGGL((k_decode_stream<D, 4>), grid, block, 0, stream, e0, e1, 0, p);
     else if (p.G <= 8)
-        hipExtLaunchKernelGGL((k_decode_fused<D, 8>), grid, block, 0, stream, e0, e1, 0, p);
+        hipExtLaunchKernelGGL((k_decode_stream<D, 8>), grid, block, 0, stream, e0, e1, 0, p);
     else
-        hipExtLaunchKernelGGL((k_decode_fused<D, 16>), grid, block, 0, stream, e0, e1, 0, p);
+        hipExtLaunchKernelGGL((k_decode_stream<D, 16>), grid, block, 0, stream, e0, e1, 0, p);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
                                hipEvent_t e1)
 {
-    return p.D == 64 ? launch_fused_d<64>(p, stream, e0, e1)
-                     : launch_fused_d<128>(p, stream, e0, e1);
+    return p.D == 64 ? launch_stream_d<64>(p, stream, e0, e1)
+                     : launch_stream_d<128>(p, stream, e0, e1);
 }
 
 hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream)
@@ -661,6 +904,27 @@ hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream)
     else
         hipLaunchKernelGGL(k_decode_merge<128>, grid, block, 0, stream, p);
     return hipGetLastError();
+}
+
+int decode_resident_waves(int device, int D, int G)
+{
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return 0;
+    const void *k;
+    if (G <= 1)
+        k = D == 64 ? (const void *)k_decode_stream<64, 1> : (const void *)k_decode_stream<128, 1>;
+    else if (G <= 2)
+        k = D == 64 ? (const void *)k_decode_stream<64, 2> : (const void *)k_decode_stream<128, 2>;
+    else if (G <= 4)
+        k = D == 64 ? (const void *)k_decode_stream<64, 4> : (const void *)k_decode_stream<128, 4>;
+    else if (G <= 8)
+        k = D == 64 ? (const void *)k_decode_stream<64, 8> : (const void *)k_decode_stream<128, 8>;
+    else
+        k = D == 64 ? (const void *)k_decode_stream<64, 16> : (const void *)k_decode_stream<128, 16>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64, 0) != hipSuccess)
+        return 0;
+    return cus * per_cu;
 }
 
 hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,

@@ -22,12 +22,11 @@ struct DecodeParams {
     uint16_t *out;             // [A, Hq, D]
     int64_t o_sa, o_sh;
     float *qrot;      // workspace [A, Hq, D]      rotated queries, FP32
-    float *part_o;    // workspace [A, Hq, NS, D]  per-split unnormalized outputs
-    float *part_ml;   // workspace [A, Hq, NS, 2]  per-split (max, sum) in the log2 domain
+    float *part_o;    // workspace [slots, G, D]  per (segment, wave) unnormalized outputs
+    float *part_ml;   // workspace [slots, G, 2]  per (segment, wave) (max, sum), log2 domain
     int32_t *status;  // optional device status word
     int32_t A, S, C, Hq, Hkv, D, G;
-    int32_t NS;        // splits per row in the grid
-    int32_t kps;       // keys per split
+    int32_t NS;        // waves of the decode launch (slots = A * Hkv + NS)
     float scale_log2;  // log2(e) / sqrt(D)
     float inv_freq[kMaxHalfDim];
 };
@@ -45,7 +44,9 @@ hipError_t launch_rope_store(const DecodeParams &p, hipStream_t stream);
 // e0 / e1: optional events stamped at the kernel's start and end.
 hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
                                hipEvent_t e1);
-// Cross-split merge -> BF16 output (one wave per entry and query head).
+// Resident wave slots of the decode kernel variant on a device (0 on error).
+int decode_resident_waves(int device, int D, int G);
+// Cross-wave merge -> BF16 output (one wave per entry and query head).
 hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream);
 // Readable one-wave-per-(entry, query head) attention straight to the output.
 hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,

@@ -8,7 +8,11 @@
 // storage, unsupported operations fail explicitly).
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
+#include <map>
+#include <mutex>
+#include <tuple>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -169,25 +173,19 @@ void fill_inv_freq(float *inv, double base, int D)
         inv[i] = (float)std::pow(base, -2.0 * (double)i / (double)D);
 }
 
-constexpr int kDefaultKeysPerSplit = 256;
-
-mllm_status resolve_opts(const mllm_decode_opts *opts, int *kps, int *kernel)
+mllm_status resolve_opts(const mllm_decode_opts *opts, int *waves, int *kernel)
 {
-    *kps = kDefaultKeysPerSplit;
+    *waves = 0;
     *kernel = 0;
     if (!opts)
         return MLLM_OK;
     for (int i = 0; i < 4; ++i)
         if (opts->reserved[i] != 0)
             return fail(MLLM_ERR_INVALID_ARG, "reserved option fields must be zero");
-    if (opts->keys_per_split != 0) {
-        if (opts->keys_per_split < 64 || opts->keys_per_split > 65536 ||
-            opts->keys_per_split % 64 != 0)
-            return fail(MLLM_ERR_INVALID_ARG,
-                        "keys_per_split %d must be a multiple of 64 in [64, 65536]",
-                        opts->keys_per_split);
-        *kps = opts->keys_per_split;
-    }
+    if (opts->waves < 0 || opts->waves > MLLM_MAX_WAVES)
+        return fail(MLLM_ERR_INVALID_ARG, "waves %d must be 0 (device default) or in [1, %d]",
+                    opts->waves, MLLM_MAX_WAVES);
+    *waves = opts->waves;
     if (opts->kernel != 0 && opts->kernel != 1)
         return fail(MLLM_ERR_INVALID_ARG, "kernel %d unknown (0 tuned, 1 readable)",
                     opts->kernel);
@@ -195,9 +193,26 @@ mllm_status resolve_opts(const mllm_decode_opts *opts, int *kps, int *kernel)
     return MLLM_OK;
 }
 
-int splits_for(int max_position, int kps)
+// Waves a decode launch divides the keys among: the option, else the device's
+// resident wave slots for the kernel variant (queried once per device/shape).
+int launch_waves(int requested, int device, int D, int G)
 {
-    return (max_position + kps) / kps;  // ceil((max_position + 1) / kps)
+    if (requested > 0)
+        return requested;
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int>, int> cache;
+    const int gcls = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+    std::lock_guard<std::mutex> lock(mu);
+    auto key = std::make_tuple(device, D, gcls);
+    auto it = cache.find(key);
+    if (it != cache.end())
+        return it->second;
+    int nw = mllm::decode_resident_waves(device, D, G);
+    if (nw <= 0)
+        nw = 2048;
+    nw = std::min(nw, MLLM_MAX_WAVES);
+    cache[key] = nw;
+    return nw;
 }
 
 mllm_status check_device_current(int device)
@@ -373,13 +388,13 @@ mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32
     if (max_position < -1 || max_position >= d.capacity)
         return fail(MLLM_ERR_INVALID_ARG, "max_position %d outside [-1, capacity)",
                     max_position);
-    int kps, kernel;
-    mllm_status st = resolve_opts(opts, &kps, &kernel);
+    int waves, kernel;
+    mllm_status st = resolve_opts(opts, &waves, &kernel);
     if (st)
         return st;
-    const int maxp = max_position < 0 ? d.capacity - 1 : max_position;
-    const int ns = splits_for(maxp, kps);
-    *bytes = mllm::decode_workspace_layout(A, h_q, d.h_kv, d.head_dim, ns).total;
+    // the slot count covers any wave count up to the option or the maximum
+    const int nw = waves > 0 ? waves : MLLM_MAX_WAVES;
+    *bytes = mllm::decode_workspace_layout(A, h_q, d.h_kv, d.head_dim, nw).total;
     return ok();
 }
 
@@ -418,8 +433,8 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     mllm_status st = check_rope(rope, D);
     if (st)
         return st;
-    int kps, kernel;
-    st = resolve_opts(opts, &kps, &kernel);
+    int waves, kernel;
+    st = resolve_opts(opts, &waves, &kernel);
     if (st)
         return st;
 
@@ -433,11 +448,9 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     if (A > 0 && (!positions_dev || !cache_rows_dev))
         return fail(MLLM_ERR_INVALID_ARG, "positions and cache_rows must be non-null");
 
-    int maxp = d.capacity - 1;
     if (host_mirror && A > 0) {
         const int32_t *hp = host_mirror, *hr = host_mirror + A;
         std::vector<char> seen(d.slots, 0);
-        maxp = 0;
         for (int a = 0; a < A; ++a) {
             if (hp[a] < 0 || hp[a] >= d.capacity)
                 return fail(MLLM_ERR_OUT_OF_RANGE, "positions[%d] = %d outside [0, %d)", a,
@@ -448,12 +461,10 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
             if (seen[hr[a]])
                 return fail(MLLM_ERR_INVALID_ARG, "cache row %d appears twice", hr[a]);
             seen[hr[a]] = 1;
-            if (hp[a] > maxp)
-                maxp = hp[a];
         }
     }
-    const int ns = splits_for(maxp, kps);
-    const mllm::DecodeWorkspace wl = mllm::decode_workspace_layout(A, Hq, d.h_kv, D, ns);
+    const int nw_bound = waves > 0 ? waves : MLLM_MAX_WAVES;
+    const mllm::DecodeWorkspace wl = mllm::decode_workspace_layout(A, Hq, d.h_kv, D, nw_bound);
     if (A > 0) {
         if (!workspace)
             return fail(MLLM_ERR_WORKSPACE, "workspace is null");
@@ -511,8 +522,7 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     p.Hkv = d.h_kv;
     p.D = D;
     p.G = G;
-    p.NS = ns;
-    p.kps = kps;
+    p.NS = launch_waves(waves, d.device, D, G);
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     fill_inv_freq(p.inv_freq, rope->base, D);
 
@@ -591,8 +601,8 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
     mllm_status st = check_rope(rope, D);
     if (st)
         return st;
-    int kps_unused, kernel;
-    if ((st = resolve_opts(opts, &kps_unused, &kernel)))
+    int waves_unused, kernel;
+    if ((st = resolve_opts(opts, &waves_unused, &kernel)))
         return st;
     Range rq, rk, rv, ro;
     const int64_t sq[4] = {A, T, Hq, D}, skv[4] = {A, T, d.h_kv, D};

@@ -45,17 +45,17 @@ class DecodeRun:
     def snapshot(self):
         return self.Kc.clone(), self.Vc.clone()
 
-    def run(self, kernel=0, keys_per_split=0, mirror=True, max_position=-1):
+    def run(self, kernel=0, waves=0, mirror=True, max_position=-1):
         A, Hq, _ = self.q.shape
         if mirror and A:
             max_position = int(self.pos_h.max())
-        nbytes = pac.decode_workspace_size(self.cache, A, Hq, max_position, keys_per_split, kernel)
+        nbytes = pac.decode_workspace_size(self.cache, A, Hq, max_position, waves, kernel)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.q.device)
         hm = np.concatenate([self.pos_h, self.rows_h]) if mirror else None
         pac.decode_rope_store_attn(self.cache, 0, self.q, self.k_new, self.v_new, self.pos,
                                    self.rows, self.out, self.ws, self.cfg["base"],
                                    host_mirror=hm, status=self.status,
-                                   keys_per_split=keys_per_split, kernel=kernel)
+                                   waves=waves, kernel=kernel)
         torch.cuda.synchronize()
         return self.out
 

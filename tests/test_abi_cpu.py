@@ -144,9 +144,11 @@ def test_decode_rejections_before_device():
     expect(call_decode(fc, ws_bytes=16), "WORKSPACE")
     # options
     o = pac.DecodeOpts()
-    o.keys_per_split = 100
+    o.waves = -1
     expect(call_decode(fc, opts=o), "INVALID_ARG")
-    o.keys_per_split, o.kernel = 0, 5
+    o.waves = pac.MAX_WAVES + 1
+    expect(call_decode(fc, opts=o), "INVALID_ARG")
+    o.waves, o.kernel = 0, 5
     expect(call_decode(fc, opts=o), "INVALID_ARG")
 
 
@@ -183,9 +185,13 @@ def test_decode_zero_entries_is_noop():
 
 def test_workspace_size_and_rows():
     fc = FakeCache()
-    a = pac.decode_workspace_size(fc.cache, 4, 4, -1, keys_per_split=64)
-    b = pac.decode_workspace_size(fc.cache, 4, 4, 10, keys_per_split=64)
-    assert a > b > 0
+    # one size for every position; the default covers any wave count
+    a = pac.decode_workspace_size(fc.cache, 4, 4, -1, waves=64)
+    b = pac.decode_workspace_size(fc.cache, 4, 4, 10, waves=64)
+    full = pac.decode_workspace_size(fc.cache, 4, 4, -1)
+    assert a == b > 0 and full > a
+    G, D = 4 // fc.Hkv, fc.D
+    assert full >= 4 * 4 * D * 4 + (4 * fc.Hkv + pac.MAX_WAVES) * G * (D + 2) * 4
     with pytest.raises(pac.MllmError):
         pac.decode_workspace_size(fc.cache, 4, 3, -1)
     with pytest.raises(pac.MllmError):

@@ -51,14 +51,16 @@ HEADS = [(4, 4), (4, 2), (8, 2), (16, 2), (32, 2), (6, 2)]
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("heads", HEADS, ids=[f"{q}x{k}" for q, k in HEADS])
-@pytest.mark.parametrize("kps", [64, 256, 1024])
-def test_edge_positions(D, heads, kps):
+@pytest.mark.parametrize("waves", [1, 5, 64, 0], ids=["w1", "w5", "w64", "wdev"])
+def test_edge_positions(D, heads, waves):
+    """Every tile boundary, with one wave walking all segments, waves splitting
+    segments mid-way, and the device default (more waves than tiles)."""
     Hq, Hkv = heads
-    H.log(f"edge D={D} Hq={Hq} Hkv={Hkv} kps={kps}")
-    cfg, inp = small_case(D, Hq, Hkv, EDGE_POS, C=640, seed=D + Hq + kps)
+    H.log(f"edge D={D} Hq={Hq} Hkv={Hkv} waves={waves}")
+    cfg, inp = small_case(D, Hq, Hkv, EDGE_POS, C=640, seed=D + Hq + waves)
     run = H.DecodeRun(inp, cfg)
     Kpre, Vpre = run.snapshot()
-    run.run(kernel=0, keys_per_split=kps)
+    run.run(kernel=0, waves=waves)
     H.full_parity(run, Kpre, Vpre)
     H.check_untouched(run, Kpre, Vpre, list(zip(run.rows_h, run.pos_h)))
 
@@ -96,8 +98,8 @@ def test_sentinel_never_read():
             assert torch.equal(run.out.view(torch.int16), ref.view(torch.int16))
 
 
-def test_idempotent_deterministic_split_invariant():
-    H.log("idempotence / determinism / split invariance")
+def test_idempotent_deterministic_wave_invariant():
+    H.log("idempotence / determinism / wave-count invariance")
     cfg, inp = small_case(128, 32, 8, [100, 2047, 900, 4095, 1], C=4096, S=6, seed=21)
     run = H.DecodeRun(inp, cfg)
     Kpre, Vpre = run.snapshot()
@@ -108,10 +110,10 @@ def test_idempotent_deterministic_split_invariant():
     assert torch.equal(K1.view(torch.int16), run.Kc.view(torch.int16))
     assert torch.equal(V1.view(torch.int16), run.Vc.view(torch.int16))
     outs = []
-    for kps in (64, 128, 512, 4096):
-        outs.append(H.workloads.bits(run.run(keys_per_split=kps)))
+    for waves in (1, 3, 100, 4096):
+        outs.append(H.workloads.bits(run.run(waves=waves)))
     for o in outs[1:]:
-        H.check_output(o, outs[0], "split invariance")
+        H.check_output(o, outs[0], "wave-count invariance")
     H.full_parity(run, Kpre, Vpre)
 
 
