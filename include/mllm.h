@@ -93,20 +93,23 @@ typedef struct {
 
 /* Optional knobs of the decode and prefill calls (NULL = defaults). */
 typedef struct {
-    /* Decode: waves that share the keys of all (entry, kv head) segments, each
-     * taking the same number of 32-key tiles.  0 = the device's resident
-     * waves (one per wave slot); else 1 .. 8192.  Ignored by prefill. */
+    /* Decode: waves that share the 32-key tiles of all (entry, kv head)
+     * segments.  Waves run in groups of up to 8, one per kv head of a head
+     * group, and each group takes an equal share of the (entry, key tile)
+     * columns.  0 = the device's resident groups; else 1 .. MLLM_MAX_WAVES,
+     * rounded down to whole groups (at least one).  The output bits depend on
+     * this count.  Ignored by prefill. */
     int32_t waves;
-    int32_t kernel;         /* 0 = tuned split-K kernel, 1 = readable one-wave-per-head kernel */
-    /* NULL, or a hipEvent_t[2] that the call records on its stream right before
-     * and right after the attention kernel (the split-K kernel, or the readable
+    int32_t kernel;         /* 0 = tuned kernels, 1 = readable one-wave-per-head kernel */
+    /* NULL, or a hipEvent_t[2] that the call stamps at the start and the end
+     * of the attention kernel (the tuned kernel, or the readable
      * kernel), for per-kernel timing attribution (operator-development.md,
      * "Public interfaces": Event timing attributed per layer). */
     void *attn_events;
     int32_t reserved[4];
 } mllm_decode_opts;
 
-#define MLLM_MAX_WAVES 8192
+#define MLLM_MAX_WAVES 4096
 
 typedef struct mllm_cache mllm_cache; /* opaque */
 
@@ -188,7 +191,10 @@ mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32
  *                    the cache or the workspace (MLLM_ERR_ALIAS).
  *  workspace       : device buffer of at least mllm_decode_workspace_size()
  *                    bytes (same A, h_q and opts), 256-byte aligned,
- *                    caller-owned, contents ignored.
+ *                    caller-owned, contents ignored on entry (the call writes
+ *                    partial results there).  One workspace serves one call
+ *                    at a time: calls that overlap in time need distinct
+ *                    workspaces.
  *  status_dev      : NULL or device int32, set to 1 on a device-side index
  *                    error, never cleared by the library.
  *  stream          : hipStream_t (NULL = the null stream).
@@ -228,7 +234,7 @@ mllm_status mllm_prefill_workspace_size(const mllm_cache *cache, int32_t A, int3
  *                    distinct and logically empty, else MLLM_ERR_ROW_BUSY).
  *  1 <= T <= capacity.  On success every target row's length becomes T.
  *  opts (may be NULL): kernel 0 = matrix-core kernel, 1 = readable kernel;
- *  attn_events timestamps the attention kernel; keys_per_split is ignored.
+ *  attn_events timestamps the attention kernel; waves is ignored.
  *  Other arguments as for the decode call.
  */
 mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,

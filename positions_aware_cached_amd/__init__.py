@@ -52,7 +52,7 @@ class RopeDesc(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
-MAX_WAVES = 8192  # largest wave count a decode launch accepts
+MAX_WAVES = 4096  # largest wave count a decode launch accepts
 
 
 class DecodeOpts(ctypes.Structure):

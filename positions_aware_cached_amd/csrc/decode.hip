@@ -29,6 +29,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace mllm {
@@ -306,7 +308,7 @@ __device__ __forceinline__ void load_block(const DecodeParams &p, int c0, int la
         b.na[k] = tiles_of(p, c0 + 64 * k + lane, b.pos[k], b.row[k]);
 }
 
-// NT = Hkv * sum_a n(a) and Hkv * sum_{x < a} n(x), on every lane.
+// NT = NHG * sum_a n(a) and NHG * sum_{x < a} n(x), on every lane.
 __device__ void plan_sums(const DecodeParams &p, int a, int lane, long long &NT, long long &before)
 {
     long long s = 0, sb = 0;
@@ -319,11 +321,11 @@ __device__ void plan_sums(const DecodeParams &p, int a, int lane, long long &NT,
             sb += c0 + 64 * k + lane < a ? b.na[k] : 0;
         }
     }
-    NT = wave_sum_ll(s) * p.Hkv;
-    before = wave_sum_ll(sb) * p.Hkv;
+    NT = wave_sum_ll(s) * p.NHG;
+    before = wave_sum_ll(sb) * p.NHG;
 }
 
-// The entry holding global tile t < NT, Hkv * E(entry), and the 64-entry chunk
+// The entry holding global tile t < NT, NHG * E(entry), and the 64-entry chunk
 // around it (lane l: entry ec + l), on every lane.
 __device__ void plan_locate(const DecodeParams &p, long long t, int lane, int &a_out,
                             long long &base_out, int &ec, int &e_pos, int &e_row, int &e_na)
@@ -335,19 +337,19 @@ __device__ void plan_locate(const DecodeParams &p, long long t, int lane, int &a
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int incl = wave_incl_scan(b.na[k], lane);
-            const long long end = run + (long long)p.Hkv * incl;
+            const long long end = run + (long long)p.NHG * incl;
             const unsigned long long hit = __ballot(t < end && b.na[k] > 0);
             if (hit) {
                 const int l = __ffsll((long long)hit) - 1;
                 a_out = c0 + 64 * k + l;
-                base_out = __shfl(end - (long long)p.Hkv * b.na[k], l, 64);
+                base_out = __shfl(end - (long long)p.NHG * b.na[k], l, 64);
                 ec = c0 + 64 * k;
                 e_pos = b.pos[k];
                 e_row = b.row[k];
                 e_na = b.na[k];
                 return;
             }
-            run += (long long)p.Hkv * __shfl(incl, 63, 64);
+            run += (long long)p.NHG * __shfl(incl, 63, 64);
         }
     }
     a_out = p.A;  // not reached for t < NT
@@ -356,25 +358,37 @@ __device__ void plan_locate(const DecodeParams &p, long long t, int lane, int &a
     e_pos = e_row = e_na = 0;
 }
 
-// Waves of the plan: min(launched, NT); then wave w owns tiles
+// Groups of the plan: min(launched, NT); then group w owns tiles
 // [floor(w NT / NW), floor((w + 1) NT / NW)), never an empty range.
 __device__ __forceinline__ int plan_waves(int launched, long long NT)
 {
     return (int)min((long long)launched, NT);
 }
 
-// Wave that owns global tile t (inverse of t0(w) = floor(w NT / NW)).
+// Group that owns global tile t (inverse of t0(w) = floor(w NT / NW)).
 __device__ __forceinline__ int plan_wave_of(long long t, long long NT, int NW)
 {
     return (int)(((t + 1) * NW - 1) / NT);
 }
 
-#ifndef MLLM_DECODE_WAVES_PER_SIMD
-#define MLLM_DECODE_WAVES_PER_SIMD 2
-#endif
+// LDS of one wave: K tile, padded V tile, new key / value (rotated and raw),
+// the segment's query heads; and, shared by the group, cos/sin.
 template <int D, int GCLS>
-__global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) void k_decode_stream(
-    DecodeParams p)
+struct WaveLds {
+    static constexpr int K = kTile * D * 2, V = kTile * (D * 2 + 16), NEW = D * 2,
+                         Q = GCLS * D * 2;
+    static constexpr int bytes = K + V + 3 * NEW + Q;
+    static constexpr int shared = D * 4;  // cos[D/2], sin[D/2]
+};
+template <int D, int GCLS>
+constexpr int decode_lds_bytes(int hg)
+{
+    return hg * WaveLds<D, GCLS>::bytes + WaveLds<D, GCLS>::shared;
+}
+
+// Up to 8 waves per group (2 per SIMD); 4 with 16-column operands (1 per SIMD).
+template <int D, int GCLS>
+__global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(DecodeParams p)
 {
     using CL = Cols<GCLS>;
     constexpr int GS = CL::GS, NPART = CL::NPART, NGRP = CL::NGRP;
@@ -388,13 +402,14 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
     constexpr int VROW = D * 2 + 16;       // padded LDS row of V, bytes
     constexpr float HEADROOM = 8.0f;       // log2 growth of a column max before O is rescaled
 
-    const int w = blockIdx.x;
-    const int lane = threadIdx.x, n = lane & 15, lg = lane >> 4;
+    const int w = blockIdx.x;  // work group: one wave per kv head of a head group
+    const int wi = threadIdx.x >> 6, HG = p.HG, NHG = p.NHG;
+    const int lane = threadIdx.x & 63, n = lane & 15, lg = lane >> 4;
     const int G = p.G, Hkv = p.Hkv;
     // this lane's RoPE frequency (lanes < D / 2), read once
     const float my_freq = p.inv_freq[lane & (D / 2 - 1)];
 
-    // the plan uses min(launched waves, NT) waves, so each owns at least one tile
+    // the plan uses min(launched groups, NT) groups, so each owns at least one tile
     long long NT, unused;
     plan_sums(p, 0, lane, NT, unused);
     const int NW = plan_waves(p.NS, NT);
@@ -402,12 +417,15 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
         return;
     const long long t0 = (long long)w * NT / NW, t1 = (long long)(w + 1) * NT / NW;
 
-    __shared__ float cs[D / 2], sn[D / 2];
-    __shared__ __attribute__((aligned(16))) unsigned char klds[TK * D * 2];
-    __shared__ __attribute__((aligned(16))) unsigned char vlds[TK * VROW];
-    __shared__ __attribute__((aligned(16))) uint16_t newk[D], newv[D];  // the new token
-    __shared__ __attribute__((aligned(16))) uint16_t kraw[D];             // its key, unrotated
-    __shared__ __attribute__((aligned(16))) uint16_t qlds[GCLS * D];      // the segment's queries
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    using L = WaveLds<D, GCLS>;
+    float *cs = (float *)lds, *sn = cs + D / 2;
+    unsigned char *klds = lds + L::shared + wi * L::bytes;
+    unsigned char *vlds = klds + L::K;
+    uint16_t *newk = (uint16_t *)(vlds + L::V);  // the new token, rotated key
+    uint16_t *newv = newk + D;                   // its value
+    uint16_t *kraw = newv + D;                   // its key, unrotated
+    uint16_t *qlds = kraw + D;                   // the segment's query heads
 
     const size_t slot = (size_t)Hkv * D;
     const uint32_t slotb = (uint32_t)(slot * 2);  // bytes per position; a row fits in 2^31
@@ -439,25 +457,26 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
         j = (int)(loc - (long long)h * na);
     }
 
-    // ---- the tile in flight (nxt); cur is (a, h, j)
+    // ---- the tile in flight (nxt); cur is (a, h, j), h the head group (this
+    // wave's kv head is h HG + wi)
     int nxa = a, nxh = h, nxj = j, nxna = na, nxrow = row, nxpos = pos;
     long long nxbase = ebase;
     auto advance = [&]() {  // nxt := the tile after nxt
         if (++nxj < nxna)
             return;
         nxj = 0;
-        if (++nxh < Hkv)
+        if (++nxh < NHG)
             return;
         nxh = 0;
-        nxbase += (long long)Hkv * nxna;
+        nxbase += (long long)NHG * nxna;
         do {
             ++nxa;
             entry(nxa, nxpos, nxrow, nxna);
         } while (nxna == 0 && nxa < p.A);
     };
 
-    auto seg_base = [&](int srow, int eh, const uint16_t *blk) {
-        return (const unsigned char *)(blk + (size_t)srow * p.C * slot + (size_t)eh * D);
+    auto seg_base = [&](int srow, int hg, const uint16_t *blk) {
+        return (const unsigned char *)(blk + (size_t)srow * p.C * slot + (size_t)(hg * HG + wi) * D);
     };
 
     u32x4 kn[NB][KS], vn[VLD];
@@ -508,8 +527,9 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
     // the segment's first tile and read only after that tile has arrived
     bool own_pre = false;
     int cs_entry = -1;  // entry whose cos/sin sit in cs/sn
-    auto fetch_segment = [&](int ea, int eh, long long eb, int ena) {
+    auto fetch_segment = [&](int ea, int hg, long long eb, int ena) {
         constexpr int QCH = D / 8;  // 16-B chunks per head
+        const int eh = hg * HG + wi;
         const uint16_t *qs = p.q + ea * p.q_sa + eh * G * p.q_sh;
 #pragma unroll
         for (int c0 = 0; c0 < GCLS * QCH; c0 += 64) {
@@ -517,17 +537,18 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
             if (c < G * QCH)
                 lds_dma16(qs + (c / QCH) * p.q_sh + (c % QCH) * 8, qlds + c0 * 8);
         }
-        own_pre = eb + (long long)eh * ena + ena - 1 < t1;  // holds the last tile
+        own_pre = eb + (long long)hg * ena + ena - 1 < t1;  // holds the last tile
         if (own_pre && lane < LPK) {
             lds_dma16(p.k_new + ea * p.kn_sa + eh * p.kn_sh + lane * 8, kraw);
             lds_dma16(p.v_new + ea * p.vn_sa + eh * p.vn_sh + lane * 8, newv);
         }
     };
-    // cos/sin of entry ea's angles (ALU only; the heads of an entry share them)
+    // cos/sin of entry ea's angles, written by wave 0 for the whole group (ALU
+    // only; the heads of an entry share them)
     auto angles = [&](int ea, int epos) {
         if (ea != cs_entry) {
             cs_entry = ea;
-            if (lane < D / 2) {
+            if (wi == 0 && lane < D / 2) {
                 const float theta = __fmul_rn((float)epos, my_freq);
                 cs[lane] = (float)cos((double)theta);
                 sn[lane] = (float)sin((double)theta);
@@ -541,7 +562,8 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
     bf16x8 bq[NGRP][KS];
     float m_run, l_run;
     f32x4 O[NGRP][NDB];
-    auto start_segment = [&](int eh, int erow, int epos) {
+    auto start_segment = [&](int hg, int erow, int epos) {
+        const int eh = hg * HG + wi;
         pos = epos;
         nkeys = epos + 1;
         owner = own_pre;
@@ -605,11 +627,11 @@ __global__ __launch_bounds__(64, GCLS == 16 ? 1 : MLLM_DECODE_WAVES_PER_SIMD) vo
             for (int db = 0; db < NDB; ++db)
                 O[c][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     };
-    auto end_segment = [&](int ea, int eh) {
+    auto end_segment = [&](int ea, int hg) {
         float l = l_run;
         l += __shfl_xor(l, 16, 64);
         l += __shfl_xor(l, 32, 64);
-        const size_t sl = (size_t)(ea * Hkv + eh + w) * G;  // slot seg + w
+        const size_t sl = ((size_t)(ea * NHG + hg + w) * HG + wi) * G;  // slot (seg + w, head)
         const bool writer = n < G;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -795,18 +817,20 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
             p.status[0] = 1;
         return;
     }
-    const int G = p.G, h = hq / G, g = hq - h * G;
+    const int G = p.G, h = hq / G, g = hq - h * G, HG = p.HG, NHG = p.NHG;
+    const int hg = h / HG, wi = h - hg * HG;  // head group, wave of the group
     long long NT, before;
     plan_sums(p, a, lane, NT, before);  // NT >= 1: this entry is valid
     const int NW = plan_waves(p.NS, NT);
     const int na = (pos + kTile) / kTile;
-    const long long ts = before + (long long)h * na;
+    const long long ts = before + (long long)hg * na;
     const int wf = plan_wave_of(ts, NT, NW), wl = plan_wave_of(ts + na - 1, NT, NW);
     const int ns = wl - wf + 1;
-    const size_t s0 = (size_t)(a * p.Hkv + h + wf);  // slot of wave wf
+    // slot of the partial of group wf + x for this head
+    auto slot_of = [&](int x) { return (size_t)(a * NHG + hg + wf + x) * HG + wi; };
     float M = -INFINITY;
     for (int c = lane; c < ns; c += 64)
-        M = fmaxf(M, p.part_ml[((s0 + c) * G + g) * 2]);
+        M = fmaxf(M, p.part_ml[(slot_of(c) * G + g) * 2]);
     M = wave_max(M);
     float lw = 0.0f, O[PER];
 #pragma unroll
@@ -815,7 +839,7 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
     for (int c = 0; c < ns; c += 64) {
         float wgt = 0.0f;
         if (c + lane < ns) {
-            const float *ml = p.part_ml + ((s0 + c + lane) * G + g) * 2;
+            const float *ml = p.part_ml + (slot_of(c + lane) * G + g) * 2;
             wgt = exp2f(ml[0] - M);
             lw += wgt * ml[1];
         }
@@ -828,7 +852,7 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
                 wk[u] = __shfl(wgt, k + u, 64);
 #pragma unroll
                 for (int e = 0; e < PER; ++e)
-                    x[u][e] = p.part_o[((s0 + c + k + u) * G + g) * D + lane + 64 * e];
+                    x[u][e] = p.part_o[(slot_of(c + k + u) * G + g) * D + lane + 64 * e];
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -840,7 +864,7 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
             const float wk = __shfl(wgt, k, 64);
 #pragma unroll
             for (int e = 0; e < PER; ++e)
-                O[e] += wk * p.part_o[((s0 + c + k) * G + g) * D + lane + 64 * e];
+                O[e] += wk * p.part_o[(slot_of(c + k) * G + g) * D + lane + 64 * e];
         }
     }
     const float L = wave_sum(lw);
@@ -857,7 +881,7 @@ DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t Hkv, int6
     auto up = [](uint64_t x) { return (x + 255u) & ~uint64_t(255); };
     DecodeWorkspace w;
     w.qrot_off = 0;
-    // partial slots: at most A * Hkv segments + NS waves, G heads each
+    // partial slots: at most A * Hkv + NS (waves of the launch), G heads each
     const uint64_t slots = ((uint64_t)A * Hkv + NS) * (Hq / Hkv);
     w.part_o_off = up(w.qrot_off + (uint64_t)A * Hq * D * 4);
     w.part_ml_off = up(w.part_o_off + slots * D * 4);
@@ -871,22 +895,38 @@ hipError_t launch_rope_store(const DecodeParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <int D, int GCLS>
+static hipError_t launch_stream_v(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
+                                  hipEvent_t e1)
+{
+    const int lds = decode_lds_bytes<D, GCLS>(p.HG);
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute((const void *)k_decode_stream<D, GCLS>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   decode_lds_bytes<D, GCLS>(GCLS == 16 ? 4 : 8));
+    });
+    if (attr != hipSuccess)
+        return attr;
+    hipExtLaunchKernelGGL((k_decode_stream<D, GCLS>), dim3(p.NS), dim3(64 * p.HG), lds, stream, e0,
+                          e1, 0, p);
+    return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_stream_d(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
                                   hipEvent_t e1)
 {
-    const dim3 grid(p.NS), block(64);
     if (p.G <= 1)
-        hipExtLaunchKernelGGL((k_decode_stream<D, 1>), grid, block, 0, stream, e0, e1, 0, p);
-    else if (p.G <= 2)
-        hipExtLaunchKernelGGL((k_decode_stream<D, 2>), grid, block, 0, stream, e0, e1, 0, p);
-    else if (p.G <= 4)
-        hipExtLaunchKernelGGL((k_decode_stream<D, 4>), grid, block, 0, stream, e0, e1, 0, p);
-    else if (p.G <= 8)
-        hipExtLaunchKernelGGL((k_decode_stream<D, 8>), grid, block, 0, stream, e0, e1, 0, p);
-    else
-        hipExtLaunchKernelGGL((k_decode_stream<D, 16>), grid, block, 0, stream, e0, e1, 0, p);
-    return hipGetLastError();
+        return launch_stream_v<D, 1>(p, stream, e0, e1);
+    if (p.G <= 2)
+        return launch_stream_v<D, 2>(p, stream, e0, e1);
+    if (p.G <= 4)
+        return launch_stream_v<D, 4>(p, stream, e0, e1);
+    if (p.G <= 8)
+        return launch_stream_v<D, 8>(p, stream, e0, e1);
+    return launch_stream_v<D, 16>(p, stream, e0, e1);
 }
 
 hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
@@ -906,25 +946,37 @@ hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-int decode_resident_waves(int device, int D, int G)
+int decode_head_group(int Hkv, int G)
 {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
-        return 0;
-    const void *k;
-    if (G <= 1)
-        k = D == 64 ? (const void *)k_decode_stream<64, 1> : (const void *)k_decode_stream<128, 1>;
-    else if (G <= 2)
-        k = D == 64 ? (const void *)k_decode_stream<64, 2> : (const void *)k_decode_stream<128, 2>;
-    else if (G <= 4)
-        k = D == 64 ? (const void *)k_decode_stream<64, 4> : (const void *)k_decode_stream<128, 4>;
-    else if (G <= 8)
-        k = D == 64 ? (const void *)k_decode_stream<64, 8> : (const void *)k_decode_stream<128, 8>;
-    else
-        k = D == 64 ? (const void *)k_decode_stream<64, 16> : (const void *)k_decode_stream<128, 16>;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64, 0) != hipSuccess)
+    const int cap = G > 8 ? 4 : 8;  // waves per group: 2 per SIMD (1 with 16 columns)
+    int hg = 1;
+    while (hg * 2 <= cap && Hkv % (hg * 2) == 0)
+        hg *= 2;
+    return hg;
+}
+
+template <int D, int GCLS>
+static int resident_groups_v(int cus, int HG)
+{
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_stream<D, GCLS>, 64 * HG,
+                                                     decode_lds_bytes<D, GCLS>(HG)) != hipSuccess)
         return 0;
     return cus * per_cu;
+}
+
+int decode_resident_groups(int device, int D, int G, int HG)
+{
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return 0;
+    if (D == 64)
+        return G <= 1 ? resident_groups_v<64, 1>(cus, HG) : G <= 2 ? resident_groups_v<64, 2>(cus, HG)
+             : G <= 4 ? resident_groups_v<64, 4>(cus, HG) : G <= 8 ? resident_groups_v<64, 8>(cus, HG)
+                      : resident_groups_v<64, 16>(cus, HG);
+    return G <= 1 ? resident_groups_v<128, 1>(cus, HG) : G <= 2 ? resident_groups_v<128, 2>(cus, HG)
+         : G <= 4 ? resident_groups_v<128, 4>(cus, HG) : G <= 8 ? resident_groups_v<128, 8>(cus, HG)
+                  : resident_groups_v<128, 16>(cus, HG);
 }
 
 hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,

@@ -22,11 +22,12 @@ struct DecodeParams {
     uint16_t *out;             // [A, Hq, D]
     int64_t o_sa, o_sh;
     float *qrot;      // workspace [A, Hq, D]      rotated queries, FP32
-    float *part_o;    // workspace [slots, G, D]  per (segment, wave) unnormalized outputs
-    float *part_ml;   // workspace [slots, G, 2]  per (segment, wave) (max, sum), log2 domain
+    float *part_o;    // workspace [slots, G, D]  per (segment, group, head) unnormalized outputs
+    float *part_ml;   // workspace [slots, G, 2]  per (segment, group, head) (max, sum), log2 domain
     int32_t *status;  // optional device status word
     int32_t A, S, C, Hq, Hkv, D, G;
-    int32_t NS;        // waves of the decode launch (slots = A * Hkv + NS)
+    int32_t NS;        // work groups of the decode launch
+    int32_t HG, NHG;   // kv heads per group (one wave each), head groups per entry
     float scale_log2;  // log2(e) / sqrt(D)
     float inv_freq[kMaxHalfDim];
 };
@@ -44,8 +45,10 @@ hipError_t launch_rope_store(const DecodeParams &p, hipStream_t stream);
 // e0 / e1: optional events stamped at the kernel's start and end.
 hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
                                hipEvent_t e1);
-// Resident wave slots of the decode kernel variant on a device (0 on error).
-int decode_resident_waves(int device, int D, int G);
+// kv heads per work group for a head layout (a power of two dividing Hkv).
+int decode_head_group(int Hkv, int G);
+// Resident work groups of the decode kernel variant on a device (0 on error).
+int decode_resident_groups(int device, int D, int G, int HG);
 // Cross-wave merge -> BF16 output (one wave per entry and query head).
 hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream);
 // Readable one-wave-per-(entry, query head) attention straight to the output.

@@ -193,26 +193,27 @@ mllm_status resolve_opts(const mllm_decode_opts *opts, int *waves, int *kernel)
     return MLLM_OK;
 }
 
-// Waves a decode launch divides the keys among: the option, else the device's
-// resident wave slots for the kernel variant (queried once per device/shape).
-int launch_waves(int requested, int device, int D, int G)
+// Work groups of a decode launch (hg waves each, one per kv head of a head
+// group): the waves option divided by hg, else the device's resident groups
+// for the kernel variant (queried once per device and shape).
+int launch_groups(int requested_waves, int device, int D, int G, int hg)
 {
-    if (requested > 0)
-        return requested;
+    if (requested_waves > 0)
+        return std::max(1, requested_waves / hg);
     static std::mutex mu;
-    static std::map<std::tuple<int, int, int>, int> cache;
+    static std::map<std::tuple<int, int, int, int>, int> cache;
     const int gcls = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
     std::lock_guard<std::mutex> lock(mu);
-    auto key = std::make_tuple(device, D, gcls);
+    auto key = std::make_tuple(device, D, gcls, hg);
     auto it = cache.find(key);
     if (it != cache.end())
         return it->second;
-    int nw = mllm::decode_resident_waves(device, D, G);
-    if (nw <= 0)
-        nw = 2048;
-    nw = std::min(nw, MLLM_MAX_WAVES);
-    cache[key] = nw;
-    return nw;
+    int ng = mllm::decode_resident_groups(device, D, G, hg);
+    if (ng <= 0)
+        ng = 2048 / hg;
+    ng = std::min(ng, MLLM_MAX_WAVES / hg);
+    cache[key] = ng;
+    return ng;
 }
 
 mllm_status check_device_current(int device)
@@ -522,7 +523,9 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     p.Hkv = d.h_kv;
     p.D = D;
     p.G = G;
-    p.NS = launch_waves(waves, d.device, D, G);
+    p.HG = mllm::decode_head_group(d.h_kv, G);
+    p.NHG = d.h_kv / p.HG;
+    p.NS = launch_groups(waves, d.device, D, G, p.HG);
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     fill_inv_freq(p.inv_freq, rope->base, D);
 

@@ -191,6 +191,7 @@ def test_workspace_size_and_rows():
     full = pac.decode_workspace_size(fc.cache, 4, 4, -1)
     assert a == b > 0 and full > a
     G, D = 4 // fc.Hkv, fc.D
+    # one partial per (segment, head) and per wave of the launch, G heads each
     assert full >= 4 * 4 * D * 4 + (4 * fc.Hkv + pac.MAX_WAVES) * G * (D + 2) * 4
     with pytest.raises(pac.MllmError):
         pac.decode_workspace_size(fc.cache, 4, 3, -1)
