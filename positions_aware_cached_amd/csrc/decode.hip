@@ -946,9 +946,15 @@ hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Four kv heads per group: two groups share a compute unit, so one streams
+// while the other waits at a barrier (measured on MI355X: 4 beats 8 by 2-5 %,
+// and beats 2 and 1 on the ragged batch).
+#ifndef MLLM_HEAD_GROUP_CAP
+#define MLLM_HEAD_GROUP_CAP 4
+#endif
 int decode_head_group(int Hkv, int G)
 {
-    const int cap = G > 8 ? 4 : 8;  // waves per group: 2 per SIMD (1 with 16 columns)
+    const int cap = G > 8 ? 4 : MLLM_HEAD_GROUP_CAP;
     int hg = 1;
     while (hg * 2 <= cap && Hkv % (hg * 2) == 0)
         hg *= 2;
