@@ -32,6 +32,23 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// One 16-B global -> LDS load per active lane: lane l's bytes land at
+// lds_base + 16 l (the LDS base is wave-uniform).
+__device__ __forceinline__ void lds_dma16(const void *g, void *lds_base)
+{
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+// Two FP32 values -> packed BF16 (round to nearest even) with the gfx950
+// conversion instruction; used for matrix-core operands (finite values).
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 __device__ __forceinline__ uint32_t f2bf(float f)
 {
     uint32_t u = __float_as_uint(f);
@@ -168,15 +185,15 @@ __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const 
 // The rotated query and the weights enter the matrix cores as BF16 (rounded
 // to nearest even); products accumulate in FP32; the output is rounded once.
 template <int D>
-__global__ __launch_bounds__(256) void k_prefill_mfma(PrefillParams p, const float2 *table)
+__global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const float2 *table)
 {
     constexpr int BM = 128, BN = 64;
     constexpr int KS = D / 16;              // QK k-steps
     constexpr int NDB = D / 32;             // PV dim blocks
-    constexpr int ROW = D * 2 + 16;         // padded LDS row, bytes
+    constexpr int ROW = D * 2;              // LDS row of a key, bytes (chunk-swizzled)
     constexpr int CPR = D / 8;              // 16-B chunks per key row
-    constexpr int KPL = 256 / CPR;          // key rows per workgroup load instruction
-    constexpr int LPT = BN / KPL;           // loads per thread per tile and tensor
+    constexpr int RPI = 64 / CPR;           // key rows per 1-KiB LDS-DMA instruction
+    constexpr int NI = BN / RPI;            // DMA instructions per tile and tensor
     constexpr float HEADROOM = 8.0f;
 
     const int nqt = (p.T + BM - 1) / BM;
@@ -196,8 +213,15 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillParams p, const flo
     const int nkeys = min(q0 + BM, p.T);
     const int ntiles = (nkeys + BN - 1) / BN;
 
+    // K and V tiles, double-buffered, filled straight from memory by LDS-DMA.
+    // Chunk c of key row r sits at chunk slot c ^ (r % CPR) of its LDS row, so
+    // the operand reads below (32 rows at one chunk, and the transposing V
+    // reads) spread over all banks without padding.
     __shared__ __attribute__((aligned(16))) unsigned char klds[2][BN * ROW];
     __shared__ __attribute__((aligned(16))) unsigned char vlds[2][BN * ROW];
+    auto lds_off = [](int r, int byte) {  // byte offset of (row r, byte) in a tile
+        return r * ROW + ((((byte >> 4) ^ r) & (CPR - 1)) << 4) + (byte & 15);
+    };
 
     const size_t slot = (size_t)p.Hkv * D;
     const size_t rb = (size_t)row * p.C * slot + (size_t)kv * D;
@@ -205,25 +229,20 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillParams p, const flo
     const unsigned char *vb = (const unsigned char *)(p.vc + rb);
     const uint32_t slotb = (uint32_t)(slot * 2);
 
-    u32x4 kn[LPT], vn[LPT];
-    auto load_tile = [&](int t) {
+    // tile t into buffer buf: wave w issues DMA instructions w, w + 4, ...; lane
+    // l of instruction i fetches chunk (l % CPR) ^ (r % CPR) of key row
+    // r = RPI i + l / CPR (clamped into the prompt) into slot l % CPR
+    auto load_tile = [&](int t, int buf) {
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const uint32_t off = (uint32_t)min(t * BN + i * KPL + tid / CPR, nkeys - 1) * slotb +
-                                 (tid % CPR) * 16;
-            kn[i] = *(const u32x4 *)(kb + off);
-            vn[i] = *(const u32x4 *)(vb + off);
+        for (int i = w; i < NI; i += 4) {
+            const int r = i * RPI + lane / CPR;
+            const uint32_t off = (uint32_t)min(t * BN + r, nkeys - 1) * slotb +
+                                 ((((lane % CPR) ^ r) & (CPR - 1)) << 4);
+            lds_dma16(kb + off, klds[buf] + i * 1024);
+            lds_dma16(vb + off, vlds[buf] + i * 1024);
         }
     };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int o = (i * KPL + tid / CPR) * ROW + (tid % CPR) * 16;
-            *(u32x4 *)(klds[buf] + o) = kn[i];
-            *(u32x4 *)(vlds[buf] + o) = vn[i];
-        }
-    };
-    load_tile(0);
+    load_tile(0, 0);
 
     // B operands of QK: the rotated query of this lane's row, dims 16 ks + 8 hh + j
     bf16x8 bq[KS];
@@ -256,7 +275,7 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillParams p, const flo
             u32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                v[e] = f2bf(x[ks][2 * e]) | (f2bf(x[ks][2 * e + 1]) << 16);
+                v[e] = pack_bf16(x[ks][2 * e], x[ks][2 * e + 1]);
             bq[ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
@@ -269,13 +288,13 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillParams p, const flo
             O[db][i] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    store_tile(0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA; the barrier covers the others
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
         const bool more = t + 1 < ntiles;
         if (more)
-            load_tile(t + 1);
+            load_tile(t + 1, buf ^ 1);
         const int k0 = t * BN;
         if (k0 <= qw + 31) {  // some key of the tile is visible to this wave's queries
             const unsigned char *kt = klds[buf], *vt = vlds[buf];
@@ -287,22 +306,30 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillParams p, const flo
                     st[b][i] = 0.0f;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const u32x4 kf = *(const u32x4 *)(kt + (b * 32 + qi) * ROW + (ks * 16 + hh * 8) * 2);
+                    const u32x4 kf = *(const u32x4 *)(kt + lds_off(b * 32 + qi, (ks * 16 + hh * 8) * 2));
                     st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
                                                                     bq[ks], st[b], 0, 0, 0);
                 }
             }
+            // raw scores; the scale (> 0) is applied inside exp2 below, so the max
+            // is taken on the raw values.  Only tiles that reach past the first
+            // query of the wave need the causal mask.
             float tmax = -INFINITY;
+            if (k0 + BN - 1 > qw) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = k0 + b * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+                        st[b][i] = key <= qrow ? st[b][i] : -INFINITY;
+                    }
+            }
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + b * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    const float v = key <= qrow ? st[b][i] * p.scale_log2 : -INFINITY;
-                    st[b][i] = v;
-                    tmax = fmaxf(tmax, v);
-                }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+                for (int i = 0; i < 16; ++i)
+                    tmax = fmaxf(tmax, st[b][i]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * p.scale_log2;
             const bool grow = tmax > m_run + HEADROOM;
             if (__any(grow)) {
                 const float m_new = grow ? tmax : m_run;
@@ -319,10 +346,12 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillParams p, const flo
                 u32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p0 = __builtin_amdgcn_exp2f(st[k2 >> 1][8 * (k2 & 1) + 2 * e] - m_run);
-                    const float p1 = __builtin_amdgcn_exp2f(st[k2 >> 1][8 * (k2 & 1) + 2 * e + 1] - m_run);
+                    const float p0 = __builtin_amdgcn_exp2f(
+                        __builtin_fmaf(st[k2 >> 1][8 * (k2 & 1) + 2 * e], p.scale_log2, -m_run));
+                    const float p1 = __builtin_amdgcn_exp2f(
+                        __builtin_fmaf(st[k2 >> 1][8 * (k2 & 1) + 2 * e + 1], p.scale_log2, -m_run));
                     l_run += p0 + p1;
-                    v[e] = f2bf(p0) | (f2bf(p1) << 16);
+                    v[e] = pack_bf16(p0, p1);
                 }
                 pb[k2] = __builtin_bit_cast(bf16x8, v);
             }
@@ -335,18 +364,17 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillParams p, const flo
                 for (int db = 0; db < NDB; ++db) {
                     const int col = (32 * db + 16 * (g & 1) + 4 * (j16 & 3)) * 2;
                     const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(vt + kbase * ROW + col));
+                        (__attribute__((address_space(3))) s16x4 *)(vt + lds_off(kbase, col)));
                     const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(vt + (kbase + 8) * ROW + col));
+                        (__attribute__((address_space(3))) s16x4 *)(vt + lds_off(kbase + 8, col)));
                     const s16x4 vv[2] = {v0, v1};
                     O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
                                                                     pb[k2], O[db], 0, 0, 0);
                 }
             }
         }
-        if (more)
-            store_tile(buf ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);  // the next tile's DMA (this wave's share)
+        __syncthreads();                // ... and every wave's; buffer buf is free again
     }
 
     l_run += __shfl_xor(l_run, 32, 64);
