@@ -197,8 +197,10 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     constexpr float HEADROOM = 8.0f;
 
     const int nqt = (p.T + BM - 1) / BM;
-    const int qt = nqt - 1 - (int)blockIdx.x;  // longest causal rows first
-    const int hq = blockIdx.y, a = blockIdx.z;
+    // blocks are dispatched x fastest: every (head, entry) of the last query
+    // tile (the longest causal rows) goes first, the first tile last
+    const int qt = nqt - 1 - (int)blockIdx.z;
+    const int hq = blockIdx.x, a = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int qi = lane & 31, hh = lane >> 5;
     const int q0 = qt * BM, qw = q0 + w * 32, qrow = qw + qi;
@@ -298,18 +300,24 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
         const int k0 = t * BN;
         if (k0 <= qw + 31) {  // some key of the tile is visible to this wave's queries
             const unsigned char *kt = klds[buf], *vt = vlds[buf];
+            // two independent 32-key blocks per k-step, so each fragment read
+            // overlaps the other block's product
             f32x16 st[2];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     st[b][i] = 0.0f;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const u32x4 kf = *(const u32x4 *)(kt + lds_off(b * 32 + qi, (ks * 16 + hh * 8) * 2));
-                    st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 kf[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    kf[b] = *(const u32x4 *)(kt + lds_off(b * 32 + qi, (ks * 16 + hh * 8) * 2));
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[b]),
                                                                     bq[ks], st[b], 0, 0, 0);
-                }
             }
             // raw scores; the scale (> 0) is applied inside exp2 below, so the max
             // is taken on the raw values.  Only tiles that reach past the first
@@ -419,7 +427,7 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream, int kernel
             hipExtLaunchKernelGGL(k_prefill_readable<128>, grid, dim3(64), 0, stream, e0, e1, 0, p,
                                   (const float2 *)table);
     } else {
-        const dim3 grid((p.T + 127) / 128, p.Hq, p.A);
+        const dim3 grid(p.Hq, p.A, (p.T + 127) / 128);
         if (p.D == 64)
             hipExtLaunchKernelGGL(k_prefill_mfma<64>, grid, dim3(256), 0, stream, e0, e1, 0, p,
                                   (const float2 *)table);
