@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--kernel", type=int, default=0, help="0 tuned stream, 1 readable")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--graph-reps", type=int, default=25,
+                    help="replays of a graph of all layers' steps (0 = skip)")
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="also time the equal-length batched prefill (0 = skip)")
     ap.add_argument("--copy-reference", action="store_true",
@@ -247,6 +249,8 @@ def main():
         },
     }
 
+    if args.graph_reps > 0:
+        res["graph"] = bench_graph(args, cache, inp, pos, rows, out, ws, mirror, cfg, kv_bytes)
     if args.prefill_steps > 0:
         res["prefill"] = bench_prefill(args, hip)
     if args.cpu_seconds > 0:
@@ -254,6 +258,41 @@ def main():
         torch.cuda.synchronize()
         res["cpu_baseline"] = cpu_baseline(args, cfg, inp, layers[0], pos_h, rows_h, out)
     print(json.dumps(res), flush=True)
+
+
+def bench_graph(args, cache, inp, pos, rows, out, ws, mirror, cfg, kv_bytes):
+    """The same step replayed from a HIP graph: one graph holds the decode
+    calls of all rotated layers (as a model's decode step would), so the
+    launch gaps between steps disappear.  Timed over whole replays."""
+    import torch
+    import positions_aware_cached_amd as pac
+    L = args.layers
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+
+    def step_all_layers():
+        for layer in range(L):
+            pac.decode_rope_store_attn(cache, layer, inp["q"], inp["k_new"], inp["v_new"], pos,
+                                       rows, out, ws, cfg["base"], host_mirror=mirror,
+                                       waves=args.waves, kernel=args.kernel)
+    with torch.cuda.stream(side):
+        step_all_layers()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_all_layers()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = args.graph_reps
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / (reps * L)
+    return {"ms_per_step": round(ms, 4), "value": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "layers_per_graph": L, "replays": reps}
 
 
 def bench_prefill(args, hip):

@@ -181,3 +181,44 @@ def test_full_config_parity(name):
         # inactive rows hold the sentinel and stayed bit-identical (checked above);
         # outputs must be finite, so no sentinel was read
         assert torch.isfinite(run.out.float()).all()
+
+
+@pytest.mark.parametrize("kernel", [0, 1], ids=["tuned", "readable"])
+def test_graph_capture_replay(kernel):
+    """The step captured into a HIP graph (it allocates nothing, memsets nothing
+    and plans on the device) replays to the eager result, bit for bit, on
+    every replay, with eager work and synchronizations in between."""
+    import positions_aware_cached_amd as pac
+    H.log(f"graph capture kernel={kernel}")
+    cfg, inp = small_case(128, 32, 8, [100, 2047, 900, 4095, 1, 333], C=4096, S=8, seed=31)
+    run = H.DecodeRun(inp, cfg)
+    Kpre, Vpre = run.snapshot()
+    want = run.run(kernel=kernel).clone()
+    Kw, Vw = run.Kc.clone(), run.Vc.clone()
+    H.full_parity(run, Kpre, Vpre)
+    A, Hq, _ = run.q.shape
+    ws = torch.empty(pac.decode_workspace_size(run.cache, A, Hq, -1, 0, kernel), dtype=torch.uint8,
+                     device="cuda")
+    mirror = np.concatenate([run.pos_h, run.rows_h])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on the capture stream
+        pac.decode_rope_store_attn(run.cache, 0, run.q, run.k_new, run.v_new, run.pos, run.rows,
+                                   run.out, ws, cfg["base"], host_mirror=mirror, kernel=kernel)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pac.decode_rope_store_attn(run.cache, 0, run.q, run.k_new, run.v_new, run.pos, run.rows,
+                                   run.out, ws, cfg["base"], host_mirror=mirror, kernel=kernel)
+    for rep in range(3):
+        run.out.zero_()
+        run.Kc.copy_(Kpre)
+        run.Vc.copy_(Vpre)
+        ws.fill_(0xA5)  # the workspace carries nothing from one call to the next
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(run.out.view(torch.int16), want.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(run.Kc.view(torch.int16), Kw.view(torch.int16)), f"replay {rep} K"
+        assert torch.equal(run.Vc.view(torch.int16), Vw.view(torch.int16)), f"replay {rep} V"
