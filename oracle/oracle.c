@@ -1,6 +1,7 @@
 /*
  * oracle.c -- plain, slow, single-threaded CPU oracle for the positions-aware
- * cached decode step and the equal-length batched prefill.
+ * cached decode step and the equal-length batched prefill (also as a chunk
+ * appended at per-row start positions).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
  * baseline leg of the benchmark may load this library.  The product path
@@ -38,6 +39,9 @@
  *    i.e. it is the BF16-rounded rotated key.
  *  - Position p is the slot the token is stored in; attention covers the
  *    p + 1 keys 0..p inclusive.
+ *  - A prefill chunk of T tokens appended at a nonzero start s (rows that
+ *    already hold s tokens) is T decode steps at positions s..s+T-1 taken
+ *    together; the pages only define the start-0 case (empty rows).
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
  * (see oracle/build.py).  -ffp-contract=off keeps every product rounded.
@@ -276,10 +280,22 @@ int orc_decode_step(int A, int S, int C, int Hq, int Hkv, int D, double base,
  *  the cache is always stored for all T tokens.  Outputs for positions not in
  *  the list are left as they were.
  */
-int orc_prefill(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
-                const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
-                const int32_t *rows, uint16_t *Kc, uint16_t *Vc, uint16_t *out,
-                const int32_t *t_list, int n_t)
+/*
+ * Chunk of T tokens appended to each entry's row at its own start position
+ * s = starts[a] (starts == NULL: every s = 0, the equal-length prefill into
+ * empty rows of "Tensor ownership boundary").  The pages define the decode
+ * step (one token at a per-row position, attention over the row's cached
+ * prefix) and the equal-length prefill; a chunk at a nonzero start is read
+ * here as T decode steps at positions s .. s+T-1 taken together: every token
+ * t is rotated at s + t and stored at slot s + t of its row, then query t
+ * attends keys 0 .. s + t of the row -- the prefix already in the cache and
+ * the chunk up to itself.  With T = 1 this is exactly orc_decode_step.
+ * t_list (optional) restricts which query positions t are computed.
+ */
+int orc_prefill_chunk(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
+                      const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                      const int32_t *starts, const int32_t *rows, uint16_t *Kc, uint16_t *Vc,
+                      uint16_t *out, const int32_t *t_list, int n_t)
 {
     int rc = check_shapes(A, S, C, Hq, Hkv, D);
     if (rc)
@@ -289,6 +305,10 @@ int orc_prefill(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
     rc = check_rows_unique(A, S, rows);
     if (rc)
         return rc;
+    if (starts)
+        for (int a = 0; a < A; ++a)
+            if (starts[a] < 0 || starts[a] > C - T)
+                return ORC_ERR_INDEX;
     if (t_list)
         for (int i = 0; i < n_t; ++i)
             if (t_list[i] < 0 || t_list[i] >= T)
@@ -304,21 +324,23 @@ int orc_prefill(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
     float *sn = malloc(sizeof(float) * (size_t)(D / 2));
     float *x = malloc(sizeof(float) * (size_t)D);
     float *y = malloc(sizeof(float) * (size_t)D);
-    float *e = malloc(sizeof(float) * (size_t)T);
+    float *e = malloc(sizeof(float) * (size_t)C);
     if (!inv_freq || !cs || !sn || !x || !y || !e) {
         free(inv_freq); free(cs); free(sn); free(x); free(y); free(e);
         return ORC_ERR_NOMEM;
     }
     orc_rope_inv_freq(base, D, inv_freq);
 
+    /* 1. every token of every entry: rotated K and raw V into its slot */
     for (int a = 0; a < A; ++a) {
+        const int s0 = starts ? starts[a] : 0;
         for (int t = 0; t < T; ++t) {
-            orc_rope_cos_sin(t, D, inv_freq, cs, sn);
+            orc_rope_cos_sin(s0 + t, D, inv_freq, cs, sn);
             for (int h = 0; h < Hkv; ++h) {
                 const uint16_t *k = k_new + (((long)a * T + t) * Hkv + h) * D;
                 const uint16_t *v = v_new + (((long)a * T + t) * Hkv + h) * D;
-                uint16_t *kd = Kc + rows[a] * row + (long)t * slot + (long)h * D;
-                uint16_t *vd = Vc + rows[a] * row + (long)t * slot + (long)h * D;
+                uint16_t *kd = Kc + rows[a] * row + (long)(s0 + t) * slot + (long)h * D;
+                uint16_t *vd = Vc + rows[a] * row + (long)(s0 + t) * slot + (long)h * D;
                 for (int d = 0; d < D; ++d)
                     x[d] = orc_bf16_to_f32(k[d]);
                 orc_rope_apply(x, D, cs, sn, y);
@@ -330,11 +352,13 @@ int orc_prefill(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
         }
     }
 
+    /* 2. query t of entry a: rotated at s + t, attends keys 0 .. s + t */
     int count = t_list ? n_t : T;
     for (int a = 0; a < A; ++a) {
+        const int s0 = starts ? starts[a] : 0;
         for (int i = 0; i < count; ++i) {
             int t = t_list ? t_list[i] : i;
-            orc_rope_cos_sin(t, D, inv_freq, cs, sn);
+            orc_rope_cos_sin(s0 + t, D, inv_freq, cs, sn);
             for (int hq = 0; hq < Hq; ++hq) {
                 int kv = hq / G;
                 const uint16_t *qa = q + (((long)a * T + t) * Hq + hq) * D;
@@ -344,10 +368,20 @@ int orc_prefill(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
                 const uint16_t *Kr = Kc + rows[a] * row + (long)kv * D;
                 const uint16_t *Vr = Vc + rows[a] * row + (long)kv * D;
                 long o = (((long)a * T + t) * Hq + hq) * D;
-                attend_one(y, D, Kr, Vr, slot, t, scale, e, out + o, NULL);
+                attend_one(y, D, Kr, Vr, slot, s0 + t, scale, e, out + o, NULL);
             }
         }
     }
     free(inv_freq); free(cs); free(sn); free(x); free(y); free(e);
     return ORC_OK;
+}
+
+/* Equal-length prefill into empty rows: the chunk at start 0 of every row. */
+int orc_prefill(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
+                const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                const int32_t *rows, uint16_t *Kc, uint16_t *Vc, uint16_t *out,
+                const int32_t *t_list, int n_t)
+{
+    return orc_prefill_chunk(A, T, S, C, Hq, Hkv, D, base, q, k_new, v_new, NULL, rows, Kc, Vc,
+                             out, t_list, n_t);
 }

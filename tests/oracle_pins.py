@@ -438,10 +438,104 @@ def pin_prefill_subset(orc):
     assert np.array_equal(sub[:, [0, 5, 11]], full[:, [0, 5, 11]])
 
 
+def pin_chunk_brute_force(orc):
+    """A chunk appended at nonzero per-entry starts over a random cached prefix,
+    vs float64 causal attention written out: token t of entry a is rotated at
+    s_a + t (K within 1 ulp of the float64 rotation, V exact), query t attends
+    slots 0 .. s_a + t of its row (output within 1 ulp of the float64 truth, and
+    of SDPA with an explicit boolean mask); slots outside s_a .. s_a+T-1 and
+    other rows untouched."""
+    A, T, S, C, Hq, Hkv, D, base = 3, 7, 4, 24, 4, 2, 32, 1e4
+    G = Hq // Hkv
+    c = _prefill_case(A, T, S, C, Hq, Hkv, D, seed=16)
+    rows = np.array([3, 0, 1], dtype=np.int32)
+    starts = np.array([5, 0, 17], dtype=np.int32)            # 17 + 7 == C: full row
+    Kc, Vc = c["Kc"].copy(), c["Vc"].copy()
+    out = orc.prefill(c["q"], c["k"], c["v"], rows, Kc, Vc, base, starts=starts)
+    untouched = np.ones((S, C), dtype=bool)
+    for a in range(A):
+        r, s0 = rows[a], int(starts[a])
+        untouched[r, s0:s0 + T] = False
+        for t in range(T):
+            kref = bf16_rne_f64_array(rope_f64(to_f32(c["k"][a, t]).astype(np.float64),
+                                               s0 + t, base))
+            assert ulp_dist(Kc[r, s0 + t], kref).max() <= 1
+        assert np.array_equal(Vc[r, s0:s0 + T], c["v"][a])
+        n = s0 + T
+        K = to_f32(Kc[r, :n]).astype(np.float64)               # [n, Hkv, D]
+        V = to_f32(Vc[r, :n]).astype(np.float64)
+        ref = np.zeros((T, Hq, D))
+        for t in range(T):
+            for hq in range(Hq):
+                qr = rope_f64(to_f32(c["q"][a, t, hq]).astype(np.float64), s0 + t, base)
+                sc = K[:s0 + t + 1, hq // G] @ qr / math.sqrt(D)
+                w = np.exp(sc - sc.max())
+                ref[t, hq] = (w @ V[:s0 + t + 1, hq // G]) / w.sum()
+        assert ulp_dist(out[a], bf16_rne_f64_array(ref)).max() <= 1
+        qr = np.stack([rope_f64(to_f32(c["q"][a, t]).astype(np.float64), s0 + t, base)
+                       for t in range(T)])                      # [T, Hq, D]
+        Kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+        Vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+        mask = torch.arange(n)[None, :] <= (s0 + torch.arange(T))[:, None]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qr).permute(1, 0, 2).contiguous(), Kt, Vt, attn_mask=mask)
+        assert ulp_dist(out[a], bf16_rne_f64_array(o.permute(1, 0, 2).numpy())).max() <= 1
+    assert np.array_equal(Kc[untouched], c["Kc"][untouched])
+    assert np.array_equal(Vc[untouched], c["Vc"][untouched])
+
+
+def pin_chunk_is_decode_steps(orc):
+    """A chunk of T tokens at start s equals T decode steps at positions
+    s .. s+T-1 (outputs and cache bit for bit), and splitting a chunk in two
+    changes nothing."""
+    A, T, S, C, Hq, Hkv, D, base = 2, 6, 3, 20, 4, 1, 16, 1e4
+    c = _prefill_case(A, T, S, C, Hq, Hkv, D, seed=17)
+    rows = np.array([2, 1], dtype=np.int32)
+    starts = np.array([9, 3], dtype=np.int32)
+    K1, V1 = c["Kc"].copy(), c["Vc"].copy()
+    whole = orc.prefill(c["q"], c["k"], c["v"], rows, K1, V1, base, starts=starts)
+    K2, V2 = c["Kc"].copy(), c["Vc"].copy()
+    for t in range(T):
+        dec = orc.decode_step(c["q"][:, t], c["k"][:, t], c["v"][:, t], starts + t, rows,
+                              K2, V2, base)
+        assert np.array_equal(dec, whole[:, t])
+    assert np.array_equal(K1, K2) and np.array_equal(V1, V2)
+    K3, V3 = c["Kc"].copy(), c["Vc"].copy()
+    h = 4
+    o1 = orc.prefill(c["q"][:, :h], c["k"][:, :h], c["v"][:, :h], rows, K3, V3, base,
+                     starts=starts)
+    o2 = orc.prefill(c["q"][:, h:], c["k"][:, h:], c["v"][:, h:], rows, K3, V3, base,
+                     starts=starts + h)
+    assert np.array_equal(np.concatenate([o1, o2], axis=1), whole)
+    assert np.array_equal(K1, K3) and np.array_equal(V1, V3)
+
+
+def pin_chunk_errors(orc):
+    """A chunk that would run past the row's capacity, or a negative start,
+    fails explicitly and writes nothing; start 0 is the plain prefill."""
+    A, T, S, C, Hq, Hkv, D, base = 2, 5, 2, 12, 2, 1, 16, 1e4
+    c = _prefill_case(A, T, S, C, Hq, Hkv, D, seed=18)
+    rows = [0, 1]
+    for starts in ([8, 0], [-1, 0], [12, 3]):
+        Kc, Vc = c["Kc"].copy(), c["Vc"].copy()
+        try:
+            orc.prefill(c["q"], c["k"], c["v"], rows, Kc, Vc, base, starts=starts)
+        except OracleError:
+            pass
+        else:
+            raise AssertionError(f"accepted starts {starts}")
+        assert np.array_equal(Kc, c["Kc"]) and np.array_equal(Vc, c["Vc"])
+    a = orc.prefill(c["q"], c["k"], c["v"], rows, c["Kc"].copy(), c["Vc"].copy(), base,
+                    starts=[0, 0])
+    b = orc.prefill(c["q"], c["k"], c["v"], rows, c["Kc"].copy(), c["Vc"].copy(), base)
+    assert np.array_equal(a, b)
+
+
 ALL_PINS = [
     pin_bf16_rounding, pin_rope_hand_values, pin_rope_identity_at_zero, pin_rope_norm,
     pin_rope_vs_f64, pin_rope_relative, pin_single_key, pin_uniform_softmax, pin_constant_v,
     pin_dominant_key, pin_brute_force_f64, pin_gqa_equals_mha, pin_untouched_and_sentinel,
     pin_idempotent_and_permutation, pin_errors, pin_prefill_brute_force,
-    pin_decode_after_prefill, pin_prefill_subset,
+    pin_decode_after_prefill, pin_prefill_subset, pin_chunk_brute_force,
+    pin_chunk_is_decode_steps, pin_chunk_errors,
 ]

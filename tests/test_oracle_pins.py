@@ -4,7 +4,8 @@ The mutants are textual edits of oracle/oracle.c compiled into a temporary
 library: a flipped rotation sign, a wrong RoPE frequency exponent, cycled
 instead of repeated GQA heads, a missing score scale, an exclusive causal
 bound, truncating BF16 rounding, a store into the wrong row, an unrotated
-query, a mirrored V store.  Each must fail at least one pin.
+query, a mirrored V store, a prefill chunk rotated, stored or attended as if
+it began at position 0.  Each must fail at least one pin.
 """
 import os
 
@@ -42,8 +43,16 @@ MUTANTS = [
     ("v_mirrored", "vd[d] = v[d];", "vd[d] = v[D - 1 - d];", 0),
     ("angle_in_double", "float theta = p * inv_freq[i];",
      "double theta = (double)pos * pow(10000.0, 0.0) * (double)inv_freq[i] * (1.0 + 1e-6);", 0),
-    ("prefill_position_offset", "orc_rope_cos_sin(t, D, inv_freq, cs, sn);\n            for (int h",
-     "orc_rope_cos_sin(t + 1, D, inv_freq, cs, sn);\n            for (int h", 0),
+    ("prefill_position_offset", "orc_rope_cos_sin(s0 + t, D, inv_freq, cs, sn);\n            for (int h",
+     "orc_rope_cos_sin(s0 + t + 1, D, inv_freq, cs, sn);\n            for (int h", 0),
+    ("chunk_key_rotated_from_zero", "orc_rope_cos_sin(s0 + t, D, inv_freq, cs, sn);\n            for (int h",
+     "orc_rope_cos_sin(t, D, inv_freq, cs, sn);\n            for (int h", 0),
+    ("chunk_query_rotated_from_zero", "orc_rope_cos_sin(s0 + t, D, inv_freq, cs, sn);\n            for (int hq",
+     "orc_rope_cos_sin(t, D, inv_freq, cs, sn);\n            for (int hq", 0),
+    ("chunk_keys_from_chunk_only", "attend_one(y, D, Kr, Vr, slot, s0 + t,",
+     "attend_one(y, D, Kr, Vr, slot, t,", 0),
+    ("chunk_k_stored_from_zero", "uint16_t *kd = Kc + rows[a] * row + (long)(s0 + t) * slot",
+     "uint16_t *kd = Kc + rows[a] * row + (long)t * slot", 0),
 ]
 
 
