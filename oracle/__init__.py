@@ -63,7 +63,7 @@ class Oracle:
             [i32p, u16p, u16p, u16p, i32p, ctypes.c_int]
         L.orc_prefill.restype = ctypes.c_int
         L.orc_prefill_chunk.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double] + [u16p] * 3 + \
-            [i32p, i32p, u16p, u16p, u16p, i32p, ctypes.c_int]
+            [i32p, i32p, i32p, u16p, u16p, u16p, i32p, ctypes.c_int]
         L.orc_prefill_chunk.restype = ctypes.c_int
         self.L = L
         self.path = path
@@ -130,13 +130,16 @@ class Oracle:
             raise OracleError(ERRORS.get(rc, str(rc)))
         return (out, of) if want_f32 else out
 
-    def prefill(self, q, k_new, v_new, rows, Kc, Vc, base, t_list=None, starts=None):
+    def prefill(self, q, k_new, v_new, rows, Kc, Vc, base, t_list=None, starts=None, lens=None,
+                out=None):
         """Equal-length prefill, or a chunk appended at per-entry starts.
-        q [A,T,Hq,D], k_new/v_new [A,T,Hkv,D] (uint16); starts [A] (None = 0).
+        q [A,T,Hq,D], k_new/v_new [A,T,Hkv,D] (uint16); starts [A] (None = 0);
+        lens [A] (None = T): entry a uses its first lens[a] tokens only.
 
-        Kc/Vc updated IN PLACE for all T tokens (slots start .. start+T-1).
-        Returns out [A,T,Hq,D] uint16; with t_list only those query positions
-        are computed (others stay zero).
+        Kc/Vc updated IN PLACE (slots start .. start+len-1 of each row).
+        Returns out [A,T,Hq,D] uint16 (a fresh zero array, or `out` updated in
+        place); with t_list only those query positions are computed, and rows
+        t >= lens[a] are never written.
         """
         q = _c(q, np.uint16)
         k_new = _c(k_new, np.uint16)
@@ -145,12 +148,15 @@ class Oracle:
         assert Kc.flags.c_contiguous and Vc.flags.c_contiguous
         A, T, Hq, D = q.shape
         S, C, Hkv, _ = Kc.shape
-        out = np.zeros((A, T, Hq, D), dtype=np.uint16)
+        if out is None:
+            out = np.zeros((A, T, Hq, D), dtype=np.uint16)
+        assert out.dtype == np.uint16 and out.shape == (A, T, Hq, D) and out.flags.c_contiguous
         tl = None if t_list is None else _c(t_list, np.int32)
         st = None if starts is None else _c(starts, np.int32)
+        ln = None if lens is None else _c(lens, np.int32)
         rc = self.L.orc_prefill_chunk(A, T, S, C, Hq, Hkv, D, float(base), _p(q, ctypes.c_uint16),
                                 _p(k_new, ctypes.c_uint16), _p(v_new, ctypes.c_uint16),
-                                _p(st, ctypes.c_int32),
+                                _p(st, ctypes.c_int32), _p(ln, ctypes.c_int32),
                                 _p(rows, ctypes.c_int32), _p(Kc, ctypes.c_uint16),
                                 _p(Vc, ctypes.c_uint16), _p(out, ctypes.c_uint16),
                                 _p(tl, ctypes.c_int32), 0 if tl is None else int(tl.shape[0]))

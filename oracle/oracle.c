@@ -42,6 +42,8 @@
  *  - A prefill chunk of T tokens appended at a nonzero start s (rows that
  *    already hold s tokens) is T decode steps at positions s..s+T-1 taken
  *    together; the pages only define the start-0 case (empty rows).
+ *  - A batch whose entries have different lengths is the separate
+ *    equal-length groups the pages form, run one after another.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
  * (see oracle/build.py).  -ffp-contract=off keeps every product rounded.
@@ -290,12 +292,17 @@ int orc_decode_step(int A, int S, int C, int Hq, int Hkv, int D, double base,
  * t is rotated at s + t and stored at slot s + t of its row, then query t
  * attends keys 0 .. s + t of the row -- the prefix already in the cache and
  * the chunk up to itself.  With T = 1 this is exactly orc_decode_step.
+ * lens (optional, NULL = every entry T tokens) gives entry a only its first
+ * lens[a] tokens (1 <= lens[a] <= T): the page keeps prompts of different
+ * lengths as separate groups, and a batch of several lengths here is read as
+ * those groups run one after another -- tokens t >= lens[a] are neither
+ * stored nor attended, and their output rows are not written.
  * t_list (optional) restricts which query positions t are computed.
  */
 int orc_prefill_chunk(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
                       const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
-                      const int32_t *starts, const int32_t *rows, uint16_t *Kc, uint16_t *Vc,
-                      uint16_t *out, const int32_t *t_list, int n_t)
+                      const int32_t *starts, const int32_t *lens, const int32_t *rows,
+                      uint16_t *Kc, uint16_t *Vc, uint16_t *out, const int32_t *t_list, int n_t)
 {
     int rc = check_shapes(A, S, C, Hq, Hkv, D);
     if (rc)
@@ -305,10 +312,11 @@ int orc_prefill_chunk(int A, int T, int S, int C, int Hq, int Hkv, int D, double
     rc = check_rows_unique(A, S, rows);
     if (rc)
         return rc;
-    if (starts)
-        for (int a = 0; a < A; ++a)
-            if (starts[a] < 0 || starts[a] > C - T)
-                return ORC_ERR_INDEX;
+    for (int a = 0; a < A; ++a) {
+        const int s0 = starts ? starts[a] : 0, n = lens ? lens[a] : T;
+        if (n < 1 || n > T || s0 < 0 || s0 > C - n)
+            return ORC_ERR_INDEX;
+    }
     if (t_list)
         for (int i = 0; i < n_t; ++i)
             if (t_list[i] < 0 || t_list[i] >= T)
@@ -333,8 +341,8 @@ int orc_prefill_chunk(int A, int T, int S, int C, int Hq, int Hkv, int D, double
 
     /* 1. every token of every entry: rotated K and raw V into its slot */
     for (int a = 0; a < A; ++a) {
-        const int s0 = starts ? starts[a] : 0;
-        for (int t = 0; t < T; ++t) {
+        const int s0 = starts ? starts[a] : 0, n = lens ? lens[a] : T;
+        for (int t = 0; t < n; ++t) {
             orc_rope_cos_sin(s0 + t, D, inv_freq, cs, sn);
             for (int h = 0; h < Hkv; ++h) {
                 const uint16_t *k = k_new + (((long)a * T + t) * Hkv + h) * D;
@@ -355,9 +363,11 @@ int orc_prefill_chunk(int A, int T, int S, int C, int Hq, int Hkv, int D, double
     /* 2. query t of entry a: rotated at s + t, attends keys 0 .. s + t */
     int count = t_list ? n_t : T;
     for (int a = 0; a < A; ++a) {
-        const int s0 = starts ? starts[a] : 0;
+        const int s0 = starts ? starts[a] : 0, n = lens ? lens[a] : T;
         for (int i = 0; i < count; ++i) {
             int t = t_list ? t_list[i] : i;
+            if (t >= n)
+                continue;
             orc_rope_cos_sin(s0 + t, D, inv_freq, cs, sn);
             for (int hq = 0; hq < Hq; ++hq) {
                 int kv = hq / G;
@@ -382,6 +392,6 @@ int orc_prefill(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
                 const int32_t *rows, uint16_t *Kc, uint16_t *Vc, uint16_t *out,
                 const int32_t *t_list, int n_t)
 {
-    return orc_prefill_chunk(A, T, S, C, Hq, Hkv, D, base, q, k_new, v_new, NULL, rows, Kc, Vc,
-                             out, t_list, n_t);
+    return orc_prefill_chunk(A, T, S, C, Hq, Hkv, D, base, q, k_new, v_new, NULL, NULL, rows,
+                             Kc, Vc, out, t_list, n_t);
 }

@@ -510,20 +510,50 @@ def pin_chunk_is_decode_steps(orc):
     assert np.array_equal(K1, K3) and np.array_equal(V1, V3)
 
 
+def pin_ragged_groups(orc):
+    """A batch whose entries have different lengths equals the equal-length
+    groups run one after another, bit for bit; tokens past an entry's length
+    are neither stored nor attended and their output rows are not written."""
+    A, T, S, C, Hq, Hkv, D, base = 3, 9, 4, 24, 4, 2, 16, 1e4
+    c = _prefill_case(A, T, S, C, Hq, Hkv, D, seed=19)
+    rows = np.array([1, 3, 0], dtype=np.int32)
+    starts = np.array([4, 0, 15], dtype=np.int32)
+    lens = np.array([9, 2, 5], dtype=np.int32)
+    Kc, Vc = c["Kc"].copy(), c["Vc"].copy()
+    sentinel = np.full((A, T, Hq, D), 0x7fc1, dtype=np.uint16)
+    out = orc.prefill(c["q"], c["k"], c["v"], rows, Kc, Vc, base, starts=starts, lens=lens,
+                      out=sentinel.copy())
+    K1, V1 = c["Kc"].copy(), c["Vc"].copy()
+    for a in range(A):
+        n = int(lens[a])
+        o = orc.prefill(c["q"][a:a + 1, :n], c["k"][a:a + 1, :n], c["v"][a:a + 1, :n],
+                        rows[a:a + 1], K1, V1, base, starts=starts[a:a + 1])
+        assert np.array_equal(out[a, :n], o[0])
+        assert np.array_equal(out[a, n:], sentinel[a, n:])
+    assert np.array_equal(Kc, K1) and np.array_equal(Vc, V1)
+    touched = np.zeros((S, C), dtype=bool)
+    for a in range(A):
+        touched[rows[a], starts[a]:starts[a] + lens[a]] = True
+    assert np.array_equal(Kc[~touched], c["Kc"][~touched])
+    assert np.array_equal(Vc[~touched], c["Vc"][~touched])
+    assert not np.array_equal(Kc[touched], c["Kc"][touched])
+
+
 def pin_chunk_errors(orc):
     """A chunk that would run past the row's capacity, or a negative start,
     fails explicitly and writes nothing; start 0 is the plain prefill."""
     A, T, S, C, Hq, Hkv, D, base = 2, 5, 2, 12, 2, 1, 16, 1e4
     c = _prefill_case(A, T, S, C, Hq, Hkv, D, seed=18)
     rows = [0, 1]
-    for starts in ([8, 0], [-1, 0], [12, 3]):
+    for starts, lens in (([8, 0], None), ([-1, 0], None), ([12, 3], None), ([0, 0], [0, 5]),
+                         ([0, 0], [6, 5]), ([9, 0], [4, 5])):
         Kc, Vc = c["Kc"].copy(), c["Vc"].copy()
         try:
-            orc.prefill(c["q"], c["k"], c["v"], rows, Kc, Vc, base, starts=starts)
+            orc.prefill(c["q"], c["k"], c["v"], rows, Kc, Vc, base, starts=starts, lens=lens)
         except OracleError:
             pass
         else:
-            raise AssertionError(f"accepted starts {starts}")
+            raise AssertionError(f"accepted starts {starts} lens {lens}")
         assert np.array_equal(Kc, c["Kc"]) and np.array_equal(Vc, c["Vc"])
     a = orc.prefill(c["q"], c["k"], c["v"], rows, c["Kc"].copy(), c["Vc"].copy(), base,
                     starts=[0, 0])
@@ -537,5 +567,5 @@ ALL_PINS = [
     pin_dominant_key, pin_brute_force_f64, pin_gqa_equals_mha, pin_untouched_and_sentinel,
     pin_idempotent_and_permutation, pin_errors, pin_prefill_brute_force,
     pin_decode_after_prefill, pin_prefill_subset, pin_chunk_brute_force,
-    pin_chunk_is_decode_steps, pin_chunk_errors,
+    pin_chunk_is_decode_steps, pin_ragged_groups, pin_chunk_errors,
 ]

@@ -51,6 +51,9 @@ MUTANTS = [
      "orc_rope_cos_sin(t, D, inv_freq, cs, sn);\n            for (int hq", 0),
     ("chunk_keys_from_chunk_only", "attend_one(y, D, Kr, Vr, slot, s0 + t,",
      "attend_one(y, D, Kr, Vr, slot, t,", 0),
+    ("ragged_store_whole_chunk", "for (int t = 0; t < n; ++t) {\n            orc_rope_cos_sin",
+     "for (int t = 0; t < T; ++t) {\n            orc_rope_cos_sin", 0),
+    ("ragged_query_whole_chunk", "if (t >= n)\n                continue;", "", 0),
     ("chunk_k_stored_from_zero", "uint16_t *kd = Kc + rows[a] * row + (long)(s0 + t) * slot",
      "uint16_t *kd = Kc + rows[a] * row + (long)t * slot", 0),
 ]
