@@ -48,6 +48,8 @@ def parse():
                     help="replays of a graph of all layers' steps (0 = skip)")
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="also time the equal-length batched prefill (0 = skip)")
+    ap.add_argument("--chunk-steps", type=int, default=20,
+                    help="also time the prefill chunk of mixed starts and lengths (0 = skip)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times): the reference that "
                          "scales the HBM byte counters of a profiler run")
@@ -252,7 +254,9 @@ def main():
     if args.graph_reps > 0:
         res["graph"] = bench_graph(args, cache, inp, pos, rows, out, ws, mirror, cfg, kv_bytes)
     if args.prefill_steps > 0:
-        res["prefill"] = bench_prefill(args, hip)
+        res["prefill"] = bench_prefill(args, hip, "prefill", args.prefill_steps)
+    if args.chunk_steps > 0:
+        res["chunk"] = bench_prefill(args, hip, "chunk", args.chunk_steps)
     if args.cpu_seconds > 0:
         call(0)  # a fresh layer-0 step: the oracle sample is compared with it
         torch.cuda.synchronize()
@@ -295,25 +299,34 @@ def bench_graph(args, cache, inp, pos, rows, out, ws, mirror, cfg, kv_bytes):
             "unit": "GB/s", "layers_per_graph": L, "replays": reps}
 
 
-def bench_prefill(args, hip):
-    """Equal-length batched prefill (16 prompts x 1024 tokens, 32/8/128): the
-    attention kernel's own duration from events stamped in its dispatch; the
-    store kernel runs before it in every step."""
+def bench_prefill(args, hip, name, K):
+    """Batched prefill, 32/8/128: "prefill" = 16 prompts x 1024 tokens into
+    empty rows; "chunk" = 16 rows appending chunks of 128..512 tokens at starts
+    in [0, 3072].  The attention kernel's own duration comes from events
+    stamped in its dispatch; the store kernel runs before it in every step."""
     import torch
 
     import positions_aware_cached_amd as pac
     import workloads
 
-    cfg = workloads.config("prefill")
+    cfg = workloads.config(name)
     A, T, Hq, Hkv, D = (cfg[k] for k in ("A", "T", "Hq", "Hkv", "D"))
     inp = workloads.draw_prefill(cfg, device="cuda")
     cache = pac.Cache.wrap([inp["Kc"]], [inp["Vc"]])
-    rows_h = inp["rows"]
+    if name == "chunk":
+        starts, lens, rows_h = workloads.draw_chunk_meta(cfg)
+        meta_h = np.concatenate([starts, lens, rows_h]).astype(np.int32)
+        meta = torch.as_tensor(meta_h, device="cuda")
+        label = f"chunk_16x{int(lens.min())}-{int(lens.max())}_at_{int(starts.min())}-" \
+                f"{int(starts.max())}"
+    else:
+        rows_h = inp["rows"]
+        starts, lens = np.zeros(A, dtype=np.int64), np.full(A, T, dtype=np.int64)
+        label = f"prefill_{A}x{T}"
     rows = torch.as_tensor(rows_h, device="cuda")
     out = torch.empty_like(inp["q"])
     ws = torch.empty(max(256, pac.prefill_workspace_size(cache, A, T, Hq)), dtype=torch.uint8,
                      device="cuda")
-    K = args.prefill_steps
     evs = []
     for _ in range(K):
         pair = (ctypes.c_void_p * 2)()
@@ -324,6 +337,10 @@ def bench_prefill(args, hip):
         evs.append(pair)
 
     def step(ev=None):
+        if name == "chunk":
+            pac.prefill_chunk_rope_store_attn(cache, 0, inp["q"], inp["k_new"], inp["v_new"],
+                                              meta, meta_h, out, ws, cfg["base"], attn_events=ev)
+            return
         for r in rows_h:
             cache.reset_row(int(r))
         pac.prefill_rope_store_attn(cache, 0, inp["q"], inp["k_new"], inp["v_new"], rows, rows_h,
@@ -346,17 +363,22 @@ def bench_prefill(args, hip):
         hip.hipEventDestroy(ctypes.c_void_p(pair[0]))
         hip.hipEventDestroy(ctypes.c_void_p(pair[1]))
     attn_ms = float(np.mean(ms))
-    flops = 4.0 * D * Hq * A * T * (T + 1) / 2.0            # causal QK^T and PV
-    hbm = (A * T * Hq * D * 2 * 2                            # q read, out written
-           + 2 * A * T * Hkv * D * 2 * 2)                    # k/v read, K/V stored
+    s64, n64 = starts.astype(np.float64), lens.astype(np.float64)
+    # query t of entry a sees s_a + t + 1 keys: QK^T and PV, 2 flops per MAC
+    flops = 4.0 * D * Hq * float(np.sum(n64 * s64 + n64 * (n64 + 1) / 2.0))
+    tokens = float(np.sum(n64))
+    hbm = (tokens * Hq * D * 2 * 2                           # q read, out written
+           + 2 * tokens * Hkv * D * 2 * 2                    # k/v read, K/V stored
+           + 2 * float(np.sum(s64)) * Hkv * D * 2)           # cached prefix K/V read once
     tflops = flops / (attn_ms * 1e-3) / 1e12
-    return {"workload": "prefill_16x1024", "A": A, "T": T, "h_q": Hq, "h_kv": Hkv, "head_dim": D,
-            "ms_per_step": round(wall * 1e3, 4), "attn_kernel_ms": round(attn_ms, 4),
-            "causal_gflop": round(flops / 1e9, 2),
+    return {"workload": label, "A": A, "T": T, "h_q": Hq, "h_kv": Hkv, "head_dim": D,
+            "tokens": int(tokens), "ms_per_step": round(wall * 1e3, 4),
+            "attn_kernel_ms": round(attn_ms, 4), "causal_gflop": round(flops / 1e9, 2),
+            "tokens_per_s": round(tokens / wall, 1),
             "roofline": {"kernel": "k_prefill_mfma", "bound": "mfma",
                          "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                         "traffic": measured_traffic("k_prefill_mfma", "prefill_16x1024")},
+                         "traffic": measured_traffic("k_prefill_mfma", label)},
             "hbm_gbs_step": round(hbm / wall / 1e9, 1)}
 
 

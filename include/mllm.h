@@ -213,7 +213,9 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
                                         uint64_t workspace_bytes, int32_t *status_dev,
                                         const mllm_decode_opts *opts, void *stream);
 
-/* Workspace bytes needed by mllm_prefill_rope_store_attn (may be 0). */
+/* Workspace bytes needed by mllm_prefill_rope_store_attn and
+ * mllm_prefill_chunk_rope_store_attn for A entries of (up to) T tokens and
+ * h_q query heads: a cos/sin table of A * T * head_dim / 2 float pairs. */
 mllm_status mllm_prefill_workspace_size(const mllm_cache *cache, int32_t A, int32_t T,
                                         int32_t h_q, uint64_t *bytes);
 
@@ -247,6 +249,56 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
                                          const mllm_tensor_view *out, void *workspace,
                                          uint64_t workspace_bytes, const mllm_decode_opts *opts,
                                          void *stream);
+
+/*
+ * Prefill chunk of one layer appended at per-entry start positions, with
+ * per-entry lengths.  The pages define the equal-length prefill into empty
+ * rows and the one-token cached decode step, and keep prompts of different
+ * lengths as separate groups ("Tensor ownership boundary"); this call reads a
+ * chunk of n tokens at start s as n decode steps at positions s .. s+n-1
+ * taken together, and a batch of several lengths as those equal-length groups
+ * run one after another.  For every a < A, with s = starts[a],
+ * n = lengths[a], r = rows[a], and every t < n:
+ *   K[r, s+t, h, :] = bf16(RoPE(k_new[a, t, h, :], s+t)),
+ *   V[r, s+t, h, :] = v_new[a, t, h, :];
+ *   out[a, t, hq, :] = causal GQA attention of RoPE(q[a, t, hq], s+t) over
+ *   keys 0..s+t of row r (the cached prefix and the chunk up to t), FP32
+ *   softmax, BF16 output; the products run on BF16 matrix cores as in
+ *   mllm_prefill_rope_store_attn.
+ * Tokens t >= n of an entry are ignored and out[a, t] is not written; no
+ * other cache byte is written.  starts 0 and lengths T on empty rows give
+ * exactly mllm_prefill_rope_store_attn.
+ *
+ *  chunk_dev   : device int32[3*A] = {starts[0..A), lengths[0..A),
+ *                rows[0..A)}: one array, as the page moves token, position
+ *                and row metadata in one [3, A] transfer.
+ *  chunk_host  : host int32[3*A], the same values (required).  Rows must be
+ *                in range (MLLM_ERR_OUT_OF_RANGE) and distinct
+ *                (MLLM_ERR_INVALID_ARG); 1 <= lengths[a] <= T
+ *                (MLLM_ERR_INVALID_ARG); 0 <= starts[a] and starts[a] +
+ *                lengths[a] <= capacity (MLLM_ERR_OUT_OF_RANGE).  Slots
+ *                0 .. starts[a]-1 of the row are read as the cached prefix
+ *                whatever the row's recorded length (as the decode call reads
+ *                0 .. position).  Nothing is launched when a check fails.
+ *                Device values that
+ *                disagree with the host copy make the kernels skip that
+ *                entry's stores and write NaN to its T output rows.
+ *  q [A, T, H_q, D], k_new / v_new [A, T, H_kv, D], out [A, T, H_q, D]:
+ *                T is the longest length of the batch, 1 <= T <= capacity.
+ *  workspace   : at least mllm_prefill_workspace_size(A, T, h_q) bytes.
+ *  On success each row's length becomes max(length, starts[a] + lengths[a]).
+ *  opts and the other arguments as for mllm_prefill_rope_store_attn.
+ */
+mllm_status mllm_prefill_chunk_rope_store_attn(mllm_cache *cache, int32_t layer,
+                                               const mllm_tensor_view *q,
+                                               const mllm_tensor_view *k_new,
+                                               const mllm_tensor_view *v_new,
+                                               const int32_t *chunk_dev,
+                                               const int32_t *chunk_host, int32_t A, int32_t T,
+                                               const mllm_rope_desc *rope,
+                                               const mllm_tensor_view *out, void *workspace,
+                                               uint64_t workspace_bytes,
+                                               const mllm_decode_opts *opts, void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ EXPORTS = ("mllm_abi_version", "mllm_last_error", "mllm_cache_bytes", "mllm_cach
            "mllm_cache_wrap", "mllm_cache_free", "mllm_cache_layer", "mllm_cache_get_desc",
            "mllm_cache_reset_row", "mllm_cache_row_length", "mllm_decode_workspace_size",
            "mllm_decode_rope_store_attn", "mllm_prefill_workspace_size",
-           "mllm_prefill_rope_store_attn")
+           "mllm_prefill_rope_store_attn", "mllm_prefill_chunk_rope_store_attn")
 
 
 class MllmError(RuntimeError):
@@ -92,6 +92,9 @@ def load(path=LIB_PATH):
         P(RopeDesc), P(TensorView), vp, u64, vp, P(DecodeOpts), vp]
     L.mllm_prefill_workspace_size.argtypes = [vp, i32, i32, i32, P(u64)]
     L.mllm_prefill_rope_store_attn.argtypes = [
+        vp, i32, P(TensorView), P(TensorView), P(TensorView), vp, P(i32), i32, i32,
+        P(RopeDesc), P(TensorView), vp, u64, P(DecodeOpts), vp]
+    L.mllm_prefill_chunk_rope_store_attn.argtypes = [
         vp, i32, P(TensorView), P(TensorView), P(TensorView), vp, P(i32), i32, i32,
         P(RopeDesc), P(TensorView), vp, u64, P(DecodeOpts), vp]
     _lib = L
@@ -267,6 +270,27 @@ def prefill_rope_store_attn(cache, layer, q, k_new, v_new, rows_dev, rows_host, 
         cache.handle, layer, ctypes.byref(view(q)), ctypes.byref(view(k_new)),
         ctypes.byref(view(v_new)), _ptr(rows_dev),
         ctypes.cast(rh.data_ptr(), ctypes.POINTER(ctypes.c_int32)), A, T, ctypes.byref(rope),
+        ctypes.byref(view(out)), _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        ctypes.byref(o), _stream(stream)))
+
+
+def prefill_chunk_rope_store_attn(cache, layer, q, k_new, v_new, chunk_dev, chunk_host, out,
+                                  workspace, base, kernel=0, attn_events=None, stream=None):
+    """Prefill chunk at per-entry starts and lengths (see
+    mllm_prefill_chunk_rope_store_attn).  chunk_dev: device int32 [3, A] or
+    [3*A] = (starts, lengths, rows); chunk_host: the same values on the host.
+    """
+    A, T = q.shape[0], q.shape[1]
+    rope = RopeDesc(float(base), q.shape[-1], 0)
+    o = _opts(0, kernel, attn_events)
+    ch = torch.as_tensor(chunk_host, dtype=torch.int32).contiguous()
+    if ch.numel() != 3 * A or (chunk_dev is not None and chunk_dev.numel() != 3 * A):
+        raise ValueError("chunk metadata must hold 3 * A int32 values")
+    _check(load().mllm_prefill_chunk_rope_store_attn(
+        cache.handle, layer, ctypes.byref(view(q)), ctypes.byref(view(k_new)),
+        ctypes.byref(view(v_new)), _ptr(chunk_dev),
+        ctypes.cast(ch.data_ptr(), ctypes.POINTER(ctypes.c_int32)), A, T, ctypes.byref(rope),
         ctypes.byref(view(out)), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         ctypes.byref(o), _stream(stream)))

@@ -61,10 +61,12 @@ struct PrefillParams {
     const uint16_t *v_new;  // [A, T, Hkv, D]
     int64_t q_sa, q_st, q_sh, kn_sa, kn_st, kn_sh, vn_sa, vn_st, vn_sh;
     const int32_t *rows;    // [A] device
+    const int32_t *starts;  // [A] device first position of each entry's chunk (NULL: all 0)
+    const int32_t *lens;    // [A] device tokens of each entry, 1 .. T (NULL: all T)
     uint16_t *kc, *vc;      // layer blocks [S, C, Hkv, D]
     uint16_t *out;          // [A, T, Hq, D]
     int64_t o_sa, o_st, o_sh;
-    float2 *table;          // workspace [T, D/2] (cos, sin) of positions 0 .. T-1
+    float2 *table;          // workspace [A, T, D/2] (cos, sin) of position starts[a] + t
     int32_t A, T, S, C, Hq, Hkv, D, G;
     float scale_log2;
     float inv_freq[kMaxHalfDim];

@@ -570,20 +570,25 @@ mllm_status mllm_prefill_workspace_size(const mllm_cache *cache, int32_t A, int3
     return ok();
 }
 
-mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
-                                         const mllm_tensor_view *q,
-                                         const mllm_tensor_view *k_new,
-                                         const mllm_tensor_view *v_new,
-                                         const int32_t *cache_rows_dev,
-                                         const int32_t *cache_rows_host, int32_t A, int32_t T,
-                                         const mllm_rope_desc *rope,
-                                         const mllm_tensor_view *out, void *workspace,
-                                         uint64_t workspace_bytes, const mllm_decode_opts *opts,
-                                         void *stream)
+}  // extern "C"
+
+namespace {
+
+// Both prefill calls: chunk_host == NULL is the equal-length prefill into
+// empty rows (rows_host, starts 0, lengths T); otherwise chunk_host holds
+// {starts, lengths, rows} of A entries and chunk_dev the same on the device.
+mllm_status prefill_call(mllm_cache *cache, int32_t layer, const mllm_tensor_view *q,
+                         const mllm_tensor_view *k_new, const mllm_tensor_view *v_new,
+                         const int32_t *rows_dev, const int32_t *rows_host,
+                         const int32_t *chunk_dev, const int32_t *chunk_host, int32_t A,
+                         int32_t T, const mllm_rope_desc *rope, const mllm_tensor_view *out,
+                         void *workspace, uint64_t workspace_bytes, const mllm_decode_opts *opts,
+                         void *stream)
 {
     if (!cache)
         return fail(MLLM_ERR_INVALID_ARG, "cache is null");
     const mllm_cache_desc &d = cache->desc;
+    const bool chunk = chunk_host != nullptr || chunk_dev != nullptr;
     if (layer < 0 || layer >= d.num_layers)
         return fail(MLLM_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer,
                     d.num_layers);
@@ -614,20 +619,37 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
         (st = check_view(v_new, "v_new", 4, skv, d.device, false, &rv)) ||
         (st = check_view(out, "out", 4, sq, d.device, true, &ro)))
         return st;
-    if (A > 0 && (!cache_rows_dev || !cache_rows_host))
+    if (chunk) {
+        if (A > 0 && (!chunk_dev || !chunk_host))
+            return fail(MLLM_ERR_INVALID_ARG, "chunk metadata (device and host) must be non-null");
+        rows_dev = chunk_dev ? chunk_dev + 2 * A : nullptr;
+        rows_host = chunk_host ? chunk_host + 2 * A : nullptr;
+    } else if (A > 0 && (!rows_dev || !rows_host)) {
         return fail(MLLM_ERR_INVALID_ARG, "cache_rows (device and host) must be non-null");
+    }
     std::vector<char> seen(d.slots, 0);
     for (int a = 0; a < A; ++a) {
-        const int r = cache_rows_host[a];
+        const int r = rows_host[a];
         if (r < 0 || r >= d.slots)
             return fail(MLLM_ERR_OUT_OF_RANGE, "cache_rows[%d] = %d outside [0, %d)", a, r,
                         d.slots);
         if (seen[r])
             return fail(MLLM_ERR_INVALID_ARG, "cache row %d appears twice", r);
         seen[r] = 1;
-        if (cache->length[r] != 0)
-            return fail(MLLM_ERR_ROW_BUSY, "cache row %d is not empty (length %d); reset it "
-                        "first", r, cache->length[r]);
+        if (!chunk) {
+            if (cache->length[r] != 0)
+                return fail(MLLM_ERR_ROW_BUSY, "cache row %d is not empty (length %d); reset "
+                            "it first", r, cache->length[r]);
+            continue;
+        }
+        const int s0 = chunk_host[a], n = chunk_host[A + a];
+        if (n < 1 || n > T)
+            return fail(MLLM_ERR_INVALID_ARG, "lengths[%d] = %d outside [1, T = %d]", a, n, T);
+        if (s0 < 0)
+            return fail(MLLM_ERR_OUT_OF_RANGE, "starts[%d] = %d is negative", a, s0);
+        if (s0 > d.capacity - n)
+            return fail(MLLM_ERR_OUT_OF_RANGE, "starts[%d] + lengths[%d] = %d exceeds capacity %d",
+                        a, a, s0 + n, d.capacity);
     }
     const uint64_t need = mllm::prefill_workspace_bytes(A, T, Hq, D);
     if (A > 0 && need > 0) {
@@ -640,12 +662,14 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
                         (unsigned long long)workspace_bytes, (unsigned long long)need);
     }
     const uint64_t lb = layer_bytes(d);
+    const uintptr_t meta = chunk ? (uintptr_t)chunk_dev : (uintptr_t)rows_dev;
     std::vector<Range> ranges = {
         rq, rk, rv, ro,
         Range{"cache K block", (uintptr_t)cache->k[layer], (uintptr_t)cache->k[layer] + lb, true},
         Range{"cache V block", (uintptr_t)cache->v[layer], (uintptr_t)cache->v[layer] + lb, true},
         Range{"workspace", (uintptr_t)workspace, (uintptr_t)workspace + (A ? need : 0), true},
-        Range{"cache_rows", (uintptr_t)cache_rows_dev, (uintptr_t)cache_rows_dev + 4u * A, false},
+        Range{chunk ? "chunk metadata" : "cache_rows", meta,
+              meta + (chunk ? 12u : 4u) * (uintptr_t)A, false},
     };
     if ((st = check_aliases(ranges)))
         return st;
@@ -668,7 +692,9 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
     p.vn_sa = v_new->stride[0];
     p.vn_st = v_new->stride[1];
     p.vn_sh = v_new->stride[2];
-    p.rows = cache_rows_dev;
+    p.rows = rows_dev;
+    p.starts = chunk ? chunk_dev : nullptr;
+    p.lens = chunk ? chunk_dev + A : nullptr;
     p.kc = (uint16_t *)cache->k[layer];
     p.vc = (uint16_t *)cache->v[layer];
     p.out = (uint16_t *)out->data;
@@ -691,9 +717,49 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
                                         ev ? ev[1] : nullptr);
     if (e != hipSuccess)
         return hip_fail(e, "prefill launch");
-    for (int a = 0; a < A; ++a)
-        cache->length[cache_rows_host[a]] = T;
+    for (int a = 0; a < A; ++a) {
+        const int r = rows_host[a];
+        const int end = chunk ? chunk_host[a] + chunk_host[A + a] : T;
+        if (cache->length[r] < end)
+            cache->length[r] = end;
+    }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
+                                         const mllm_tensor_view *q,
+                                         const mllm_tensor_view *k_new,
+                                         const mllm_tensor_view *v_new,
+                                         const int32_t *cache_rows_dev,
+                                         const int32_t *cache_rows_host, int32_t A, int32_t T,
+                                         const mllm_rope_desc *rope,
+                                         const mllm_tensor_view *out, void *workspace,
+                                         uint64_t workspace_bytes, const mllm_decode_opts *opts,
+                                         void *stream)
+{
+    return prefill_call(cache, layer, q, k_new, v_new, cache_rows_dev, cache_rows_host, nullptr,
+                        nullptr, A, T, rope, out, workspace, workspace_bytes, opts, stream);
+}
+
+mllm_status mllm_prefill_chunk_rope_store_attn(mllm_cache *cache, int32_t layer,
+                                               const mllm_tensor_view *q,
+                                               const mllm_tensor_view *k_new,
+                                               const mllm_tensor_view *v_new,
+                                               const int32_t *chunk_dev,
+                                               const int32_t *chunk_host, int32_t A, int32_t T,
+                                               const mllm_rope_desc *rope,
+                                               const mllm_tensor_view *out, void *workspace,
+                                               uint64_t workspace_bytes,
+                                               const mllm_decode_opts *opts, void *stream)
+{
+    if (A > 0 && (!chunk_dev || !chunk_host))
+        return fail(MLLM_ERR_INVALID_ARG, "chunk metadata (device and host) must be non-null");
+    return prefill_call(cache, layer, q, k_new, v_new, nullptr, nullptr, chunk_dev, chunk_host,
+                        A, T, rope, out, workspace, workspace_bytes, opts, stream);
 }
 
 }  // extern "C"

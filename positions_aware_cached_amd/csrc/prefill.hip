@@ -1,14 +1,18 @@
-// prefill.hip -- gfx950 kernels of the equal-length batched prefill.
+// prefill.hip -- gfx950 kernels of the batched prefill, also as a chunk
+// appended at per-entry start positions with per-entry lengths.
 //
 // microLLM-rocm ARCHITECTURE.md, "Tensor ownership boundary": equal-length
 // pending prompts run as one batch and each prefix lands in its target empty
 // shared-cache row.  Here every token's rotated K and raw V go straight to
-// (row, t) -- the same bytes the page's temporary-cache-then-copy produces --
-// and attention of query t covers keys 0..t of the row.
+// (row, s + t) -- the same bytes the page's temporary-cache-then-copy produces
+// for s = 0 -- and attention of query t covers keys 0 .. s + t of the row: the
+// prefix already cached and the chunk up to itself.  Entry a uses its first n
+// tokens only (prompts of different lengths in one batch); s = 0, n = T is the
+// page's equal-length prefill into empty rows.
 //
 //   k_prefill_store     one block per (token t, entry a): split-half RoPE of
-//                       k_new -> BF16 store, v_new bit copy; blocks of entry 0
-//                       also write the FP32 cos/sin table row of position t.
+//                       k_new -> BF16 store, v_new bit copy; the block also
+//                       writes the FP32 cos/sin table row of (a, t).
 //   k_prefill_mfma      the tuned attention: one workgroup of four waves per
 //                       (entry, query head, 128-query tile), FlashAttention-
 //                       style online softmax over 64-key tiles on the matrix
@@ -68,25 +72,42 @@ __device__ __forceinline__ void rope_pair(float x, float y, float c, float s, fl
     hi = yc + xs;
 }
 
-// workspace: cos/sin table [T][D/2] of float2 (cos, sin)
+// Entry a's chunk: cache row, first position s and token count n.  ok is false
+// when the device values disagree with the host copy the library checked.
+struct Chunk {
+    int row, s, n;
+    bool ok;
+};
+__device__ __forceinline__ Chunk chunk_of(const PrefillParams &p, int a)
+{
+    Chunk c;
+    c.row = p.rows[a];
+    c.s = p.starts ? p.starts[a] : 0;
+    c.n = p.lens ? p.lens[a] : p.T;
+    c.ok = c.row >= 0 && c.row < p.S && c.s >= 0 && c.n >= 1 && c.n <= p.T && c.s <= p.C - c.n;
+    return c;
+}
+
+// workspace: cos/sin table [A][T][D/2] of float2 (cos, sin), row (a, t) for
+// position s_a + t
 __global__ __launch_bounds__(256) void k_prefill_store(PrefillParams p, float2 *table)
 {
     const int t = blockIdx.x, a = blockIdx.y, tid = threadIdx.x;
     const int D = p.D, H = D / 2;
+    const Chunk ch = chunk_of(p, a);
+    if (!ch.ok || t >= ch.n)
+        return;  // past the entry's length, or an invalid entry: write nothing
+    const int pos = ch.s + t;
     __shared__ float cs[kMaxHalfDim], sn[kMaxHalfDim];
     if (tid < H) {
-        float theta = __fmul_rn((float)t, p.inv_freq[tid]);
+        float theta = __fmul_rn((float)pos, p.inv_freq[tid]);
         cs[tid] = (float)cos((double)theta);
         sn[tid] = (float)sin((double)theta);
-        if (a == 0)
-            table[(size_t)t * H + tid] = make_float2(cs[tid], sn[tid]);
+        table[((size_t)a * p.T + t) * H + tid] = make_float2(cs[tid], sn[tid]);
     }
     __syncthreads();
-    const int row = p.rows[a];
-    if (row < 0 || row >= p.S)
-        return;  // device rows disagree with the checked host copy: write nothing
     const size_t slot = (size_t)p.Hkv * D;
-    const size_t dst = ((size_t)row * p.C + t) * slot;
+    const size_t dst = ((size_t)ch.row * p.C + pos) * slot;
     for (int idx = tid; idx < p.Hkv * H; idx += blockDim.x) {
         const int h = idx / H, i = idx - h * H;
         const uint16_t *k = p.k_new + a * p.kn_sa + t * p.kn_st + h * p.kn_sh;
@@ -119,23 +140,27 @@ __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const 
 {
     constexpr int H = D / 2;
     const int hq = blockIdx.x, t = blockIdx.y, a = blockIdx.z, lane = threadIdx.x;
-    const int row = p.rows[a];
+    const Chunk ch = chunk_of(p, a);
     uint16_t *out = p.out + a * p.o_sa + t * p.o_st + hq * p.o_sh;
-    if (row < 0 || row >= p.S) {
+    if (!ch.ok) {  // device values disagree with the checked host copy: NaN output
 #pragma unroll
         for (int e = 0; e < D / 64; ++e)
             out[lane + 64 * e] = 0x7fc0;
         return;
     }
+    if (t >= ch.n)
+        return;
+    const int row = ch.row, last = ch.s + t;
     const int kv = hq / p.G;
     const uint16_t *qs = p.q + a * p.q_sa + t * p.q_st + hq * p.q_sh;
+    const float2 *tab = table + ((size_t)a * p.T + t) * H;
     float q[D / 64];
     if (D == 128) {
-        const float2 cs = table[(size_t)t * H + lane];
+        const float2 cs = tab[lane];
         rope_pair(bf2f(qs[lane]), bf2f(qs[lane + 64]), cs.x, cs.y, q[0], q[D / 64 - 1]);
     } else {
         const int i = lane & (H - 1);
-        const float2 cs = table[(size_t)t * H + i];
+        const float2 cs = tab[i];
         float lo, hi;
         rope_pair(bf2f(qs[i]), bf2f(qs[i + H]), cs.x, cs.y, lo, hi);
         q[0] = lane < H ? lo : hi;
@@ -147,7 +172,7 @@ __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const 
 #pragma unroll
     for (int e = 0; e < D / 64; ++e)
         o[e] = 0.0f;
-    for (int j = 0; j <= t; ++j) {
+    for (int j = 0; j <= last; ++j) {
         float part = 0.0f;
 #pragma unroll
         for (int e = 0; e < D / 64; ++e)
@@ -204,15 +229,20 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int qi = lane & 31, hh = lane >> 5;
     const int q0 = qt * BM, qw = q0 + w * 32, qrow = qw + qi;
-    const int row = p.rows[a];
-    if (row < 0 || row >= p.S) {  // device rows disagree with the checked host copy
+    const Chunk ch = chunk_of(p, a);
+    if (!ch.ok) {  // device values disagree with the checked host copy: NaN output
         if (qrow < p.T && hh == 0)
             for (int d = 0; d < D; ++d)
                 p.out[a * p.o_sa + qrow * p.o_st + hq * p.o_sh + d] = 0x7fc0;
         return;
     }
+    if (q0 >= ch.n)
+        return;  // the whole query tile lies past this entry's length
+    const int row = ch.row, s0 = ch.s, n = ch.n;
     const int kv = hq / p.G;
-    const int nkeys = min(q0 + BM, p.T);
+    // keys 0 .. s0 + n - 1 exist (the cached prefix and the chunk); the tile's
+    // last query sees up to key s0 + min(q0 + BM, n) - 1
+    const int nkeys = s0 + min(q0 + BM, n);
     const int ntiles = (nkeys + BN - 1) / BN;
 
     // K and V tiles, double-buffered, filled straight from memory by LDS-DMA.
@@ -249,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     // B operands of QK: the rotated query of this lane's row, dims 16 ks + 8 hh + j
     bf16x8 bq[KS];
     {
-        const int tq = min(qrow, p.T - 1);
+        const int tq = min(qrow, n - 1);
         const uint16_t *qs = p.q + a * p.q_sa + tq * p.q_st + hq * p.q_sh;
         float x[KS][8];
 #pragma unroll
@@ -261,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                 x[ks][2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
             }
         }
-        const float2 *cs = table + (size_t)tq * (D / 2);
+        const float2 *cs = table + ((size_t)a * p.T + tq) * (D / 2);
 #pragma unroll
         for (int ks = 0; ks < KS / 2; ++ks)
 #pragma unroll
@@ -298,7 +328,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
         if (more)
             load_tile(t + 1, buf ^ 1);
         const int k0 = t * BN;
-        if (k0 <= qw + 31) {  // some key of the tile is visible to this wave's queries
+        // some key of the tile is visible to one of this wave's queries, and the
+        // wave holds at least one query of the entry
+        if (k0 <= s0 + qw + 31 && qw < n) {
             const unsigned char *kt = klds[buf], *vt = vlds[buf];
             // two independent 32-key blocks per k-step, so each fragment read
             // overlaps the other block's product
@@ -323,13 +355,13 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
             // is taken on the raw values.  Only tiles that reach past the first
             // query of the wave need the causal mask.
             float tmax = -INFINITY;
-            if (k0 + BN - 1 > qw) {
+            if (k0 + BN - 1 > s0 + qw) {
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int key = k0 + b * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-                        st[b][i] = key <= qrow ? st[b][i] : -INFINITY;
+                        st[b][i] = key <= s0 + qrow ? st[b][i] : -INFINITY;
                     }
             }
 #pragma unroll
@@ -386,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     }
 
     l_run += __shfl_xor(l_run, 32, 64);
-    if (qrow < p.T) {
+    if (qrow < n) {
         const float inv = 1.0f / l_run;
         uint16_t *out = p.out + a * p.o_sa + qrow * p.o_st + hq * p.o_sh;
 #pragma unroll
@@ -405,9 +437,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
 
 uint64_t prefill_workspace_bytes(int64_t A, int64_t T, int64_t Hq, int64_t D)
 {
-    (void)A;
     (void)Hq;
-    return ((uint64_t)T * (D / 2) * 8u + 255u) & ~uint64_t(255);
+    return ((uint64_t)A * T * (D / 2) * 8u + 255u) & ~uint64_t(255);
 }
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream, int kernel, hipEvent_t e0,

@@ -244,3 +244,42 @@ def test_prefill_rejections_before_device():
     expect(call_prefill(fc, rows_host=(0, 9)), "OUT_OF_RANGE")
     expect(call_prefill(fc, ws=0), "WORKSPACE")
     expect(call_prefill(fc, out=fake_view([2, 16, 4, fc.D], FAKE + 0x1000000)), "ALIAS")
+
+
+def call_chunk(fc, A=2, T=16, Hq=4, meta=(0, 5, 16, 16, 0, 1), meta_dev=FAKE + 0x20000,
+               ws=FAKE + 0x40000000, ws_bytes=1 << 30, out=None):
+    D = fc.D
+    q = fake_view([A, T, Hq, D], FAKE + 0x1000000)
+    k = fake_view([A, T, fc.Hkv, D], FAKE + 0x2000000)
+    v = fake_view([A, T, fc.Hkv, D], FAKE + 0x3000000)
+    out = out or fake_view([A, T, Hq, D], FAKE + 0x4000000)
+    rope = pac.RopeDesc(1e4, D, 0)
+    mh = None if meta is None else (ctypes.c_int32 * max(1, len(meta)))(*meta)
+    return pac.load().mllm_prefill_chunk_rope_store_attn(
+        fc.cache.handle, 0, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+        ctypes.c_void_p(meta_dev), mh, A, T, ctypes.byref(rope), ctypes.byref(out),
+        ctypes.c_void_p(ws), ws_bytes, None, None)
+
+
+def test_prefill_chunk_rejections_before_device():
+    """meta = (starts[A], lengths[A], rows[A]); capacity 256, T = 16."""
+    fc = FakeCache()
+    expect(call_chunk(fc, meta=None), "INVALID_ARG")
+    expect(call_chunk(fc, meta_dev=0), "INVALID_ARG")
+    expect(call_chunk(fc, meta=(0, 5, 16, 16, 1, 1)), "INVALID_ARG")        # duplicate row
+    expect(call_chunk(fc, meta=(0, 5, 16, 16, 0, 8)), "OUT_OF_RANGE")       # row past S
+    expect(call_chunk(fc, meta=(0, 5, 16, 0, 0, 1)), "INVALID_ARG")         # length 0
+    expect(call_chunk(fc, meta=(0, 5, 17, 16, 0, 1)), "INVALID_ARG")        # length > T
+    expect(call_chunk(fc, meta=(-1, 5, 16, 16, 0, 1)), "OUT_OF_RANGE")      # negative start
+    expect(call_chunk(fc, meta=(0, 241, 16, 16, 0, 1)), "OUT_OF_RANGE")     # past capacity
+    expect(call_chunk(fc, meta=(0, 250, 16, 6, 0, 1), ws_bytes=8191), "WORKSPACE")
+    expect(call_chunk(fc, ws=FAKE + 0x40000001), "WORKSPACE")
+    expect(call_chunk(fc, meta_dev=FAKE + 0x4000000), "ALIAS")             # metadata in out
+    assert call_chunk(fc, A=0, meta=None, meta_dev=0) == 0    # no entries: a no-op
+
+
+def test_prefill_workspace_scales_with_entries():
+    fc = FakeCache()
+    for A, T in [(1, 16), (3, 16), (16, 256)]:
+        want = A * T * (fc.D // 2) * 8
+        assert pac.prefill_workspace_size(fc.cache, A, T, 4) == (want + 255) // 256 * 256

@@ -8,8 +8,9 @@ from numpy's PCG64 generator.
 
 Workload shapes follow the decode and prefill configurations the method is
 measured on: a tiny case, a Llama-3-8B-like decode batch, a ragged
-continuous batch with a long tail of positions, a long-context decode and an
-equal-length batched prefill.  The pages measure on official model workloads
+continuous batch with a long tail of positions, a long-context decode, an
+equal-length batched prefill, and a chunked prefill of mixed starts and
+lengths.  The pages measure on official model workloads
 that are not available; these seeded draws stand in for them.
 """
 import math
@@ -39,6 +40,12 @@ CONFIGS = {
     # Equal-length batched prefill: 16 prompts of 1024 tokens into empty rows.
     "prefill": dict(kind="prefill", A=16, S=16, C=2048, T=1024, Hq=32, Hkv=8, D=128,
                     base=5.0e5, sigma=1.0, rows="identity", seed=4),
+    # Chunked prefill with mixed lengths: 16 rows of a 4096-capacity cache,
+    # each appending a chunk of 128..512 tokens (uniform) at a start uniform in
+    # [0, 3072] (start 0: a fresh prompt), 32/8/128.
+    "chunk": dict(kind="chunk", A=16, S=16, C=4096, T=512, Hq=32, Hkv=8, D=128, base=5.0e5,
+                  sigma=1.0, starts=("uniform", 0, 3072), lens=("uniform", 128, 512),
+                  rows="identity", seed=5),
 }
 
 
@@ -77,6 +84,23 @@ def draw_indices(cfg):
     else:
         raise ValueError(cfg["rows"])
     return pos.astype(np.int32), rows.astype(np.int32)
+
+
+def draw_chunk_meta(cfg):
+    """starts[A], lengths[A], rows[A] (int32 numpy) of a chunk config: starts
+    and lengths uniform integers in their configured ranges (lengths clipped to
+    T, starts to C - length); rows as in draw_indices."""
+    rng = np.random.default_rng(cfg["seed"])
+    A, S, C, T = cfg["A"], cfg["S"], cfg["C"], cfg["T"]
+    _, lo, hi = cfg["lens"]
+    lens = np.minimum(rng.integers(lo, hi + 1, size=A), T)
+    _, lo, hi = cfg["starts"]
+    starts = np.minimum(rng.integers(lo, hi + 1, size=A), C - lens)
+    if cfg["rows"] == "identity":
+        rows = np.arange(A)
+    else:
+        rows = rng.permutation(S)[:A]
+    return starts.astype(np.int32), lens.astype(np.int32), rows.astype(np.int32)
 
 
 def _normal_bf16(shape, gen, device, sigma, chunk_elems=1 << 28):
@@ -147,12 +171,15 @@ def draw_cache_layers(cfg, layers, device="cuda"):
 
 
 def draw_prefill(cfg, device="cpu"):
-    """Inputs of one equal-length prefill: q [A,T,Hq,D], k_new/v_new [A,T,Hkv,D],
-    Kc/Vc [S,C,Hkv,D] with random prior bytes (the rows are logically empty),
-    rows (int32 numpy)."""
+    """Inputs of one prefill (or prefill chunk): q [A,T,Hq,D], k_new/v_new
+    [A,T,Hkv,D], Kc/Vc [S,C,Hkv,D] with random prior bytes (for a chunk, the
+    cached prefix before each start), rows (int32 numpy)."""
     A, S, C, T, Hq, Hkv, D = (cfg[k] for k in ("A", "S", "C", "T", "Hq", "Hkv", "D"))
     sigma = cfg.get("sigma", 1.0)
-    _, rows = draw_indices(cfg)
+    if cfg["kind"] == "chunk":
+        _, _, rows = draw_chunk_meta(cfg)
+    else:
+        _, rows = draw_indices(cfg)
     gen = torch.Generator(device=device)
     gen.manual_seed(2000 + cfg["seed"])
     q = _normal_bf16((A, T, Hq, D), gen, device, sigma)
