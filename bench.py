@@ -77,16 +77,18 @@ def percentile(xs, q):
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "positions_aware_cached_amd", "csrc", f)
-                  for f in ("decode.hip", "prefill.hip", "kernels.h")]
+CSRC = os.path.join(ROOT, "positions_aware_cached_amd", "csrc")
+# the sources each kernel is built from: a counter summary stays valid for a
+# kernel while these files are unchanged
+KERNEL_SOURCES = {"decode": ("decode.hip", "kernels.h"), "prefill": ("prefill.hip", "kernels.h")}
 
 
-def source_digest():
-    """Digest of the kernel sources; counter summaries are valid for one digest."""
+def source_digest(family):
+    """Digest of one kernel family's sources ("decode" or "prefill")."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -100,10 +102,13 @@ def measured_traffic(kernel, workload):
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("source_digest") != source_digest():
-        return None
     e = c.get("kernels", {}).get(f"{kernel}@{workload}")
-    return None if e is None else e.get("hbm_bytes_per_launch")
+    if e is None:
+        return None
+    family = "decode" if kernel.startswith("k_decode") else "prefill"
+    if e.get("source_digest") != source_digest(family):
+        return None
+    return e.get("hbm_bytes_per_launch")
 
 
 def copy_reference():
@@ -299,6 +304,17 @@ def bench_graph(args, cache, inp, pos, rows, out, ws, mirror, cfg, kv_bytes):
             "unit": "GB/s", "layers_per_graph": L, "replays": reps}
 
 
+def prefill_label(name):
+    """Workload name of a prefill leg, with its sizes."""
+    import workloads
+    cfg = workloads.config(name)
+    if name == "chunk":
+        starts, lens, _ = workloads.draw_chunk_meta(cfg)
+        return (f"chunk_{cfg['A']}x{int(lens.min())}-{int(lens.max())}_at_{int(starts.min())}-"
+                f"{int(starts.max())}")
+    return f"prefill_{cfg['A']}x{cfg['T']}"
+
+
 def bench_prefill(args, hip, name, K):
     """Batched prefill, 32/8/128: "prefill" = 16 prompts x 1024 tokens into
     empty rows; "chunk" = 16 rows appending chunks of 128..512 tokens at starts
@@ -313,16 +329,14 @@ def bench_prefill(args, hip, name, K):
     A, T, Hq, Hkv, D = (cfg[k] for k in ("A", "T", "Hq", "Hkv", "D"))
     inp = workloads.draw_prefill(cfg, device="cuda")
     cache = pac.Cache.wrap([inp["Kc"]], [inp["Vc"]])
+    label = prefill_label(name)
     if name == "chunk":
         starts, lens, rows_h = workloads.draw_chunk_meta(cfg)
         meta_h = np.concatenate([starts, lens, rows_h]).astype(np.int32)
         meta = torch.as_tensor(meta_h, device="cuda")
-        label = f"chunk_16x{int(lens.min())}-{int(lens.max())}_at_{int(starts.min())}-" \
-                f"{int(starts.max())}"
     else:
         rows_h = inp["rows"]
         starts, lens = np.zeros(A, dtype=np.int64), np.full(A, T, dtype=np.int64)
-        label = f"prefill_{A}x{T}"
     rows = torch.as_tensor(rows_h, device="cuda")
     out = torch.empty_like(inp["q"])
     ws = torch.empty(max(256, pac.prefill_workspace_size(cache, A, T, Hq)), dtype=torch.uint8,

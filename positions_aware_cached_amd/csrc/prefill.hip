@@ -222,10 +222,29 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     constexpr float HEADROOM = 8.0f;
 
     const int nqt = (p.T + BM - 1) / BM;
-    // blocks are dispatched x fastest: every (head, entry) of the last query
-    // tile (the longest causal rows) goes first, the first tile last
-    const int qt = nqt - 1 - (int)blockIdx.z;
-    const int hq = blockIdx.x, a = blockIdx.y;
+    // Work groups are handed to the eight XCDs in turn (group b to XCD b % 8),
+    // and each XCD has its own L2.  The G query heads of a kv head read the same
+    // K/V tiles, so all blocks of one (entry, kv head) pair go to one XCD: pair
+    // i lives on XCD i % 8.  Each XCD runs its blocks longest query tile first
+    // (the tile rank is the slowest index), its pairs and heads within a rank.
+    int qt, hq, a;
+    {
+        const int b = blockIdx.x, npairs = p.A * p.Hkv;
+        if ((npairs & 7) == 0) {
+            const int x = b & 7, j = b >> 3;
+            const int per = (npairs >> 3) * p.G;  // blocks of one tile rank on one XCD
+            const int rank = j / per, rem = j - rank * per;
+            const int pair = (rem / p.G) * 8 + x;
+            a = pair / p.Hkv;
+            hq = (pair - a * p.Hkv) * p.G + rem % p.G;
+            qt = nqt - 1 - rank;
+        } else {
+            const int per = p.Hq * p.A, rank = b / per, rem = b - rank * per;
+            a = rem / p.Hq;
+            hq = rem - a * p.Hq;
+            qt = nqt - 1 - rank;
+        }
+    }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int qi = lane & 31, hh = lane >> 5;
     const int q0 = qt * BM, qw = q0 + w * 32, qrow = qw + qi;
@@ -458,7 +477,7 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream, int kernel
             hipExtLaunchKernelGGL(k_prefill_readable<128>, grid, dim3(64), 0, stream, e0, e1, 0, p,
                                   (const float2 *)table);
     } else {
-        const dim3 grid(p.Hq, p.A, (p.T + 127) / 128);
+        const dim3 grid(p.Hq * p.A * ((p.T + 127) / 128));
         if (p.D == 64)
             hipExtLaunchKernelGGL(k_prefill_mfma<64>, grid, dim3(256), 0, stream, e0, e1, 0, p,
                                   (const float2 *)table);
