@@ -194,6 +194,24 @@ __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const 
 
 
 // ---------------------------------------------------------------- tuned
+
+// LDS slot of the 16-B chunks of key row r: chunk c sits at slot c ^ swz(r).
+// Only r % 16 matters.  Within each aligned group of four rows the slot bits
+// 1-2 and the bits 2-3 each take all four values, and the group constant sets
+// bits 0 and 3, which keeps the 16 rows' patterns distinct (also modulo 8): so
+// the K operand reads (16 consecutive rows at one chunk) and the transposing V
+// reads (4 rows x 4 chunks per 32 lanes) both hit every bank once per pass,
+// for 32 as for 64 four-byte banks.
+__device__ __forceinline__ int swz(int r)
+{
+    const int b0 = r & 1, b1 = (r >> 1) & 1, g = (r >> 2) & 3;
+    return ((b0 << 1) | (b1 << 2) | ((b0 ^ b1) << 3)) ^ ((g & 1) | ((g >> 1) << 3));
+}
+
+template <int B>
+struct Buf {
+    static constexpr int value = B;
+};
 //
 // One workgroup (4 waves, wave w owns queries q0 + 32 w .. + 31) per (entry a,
 // query head hq, query tile q0 .. q0 + 127); the kv head is hq / G.  Key tiles
@@ -265,14 +283,10 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     const int ntiles = (nkeys + BN - 1) / BN;
 
     // K and V tiles, double-buffered, filled straight from memory by LDS-DMA.
-    // Chunk c of key row r sits at chunk slot c ^ (r % CPR) of its LDS row, so
-    // the operand reads below (32 rows at one chunk, and the transposing V
-    // reads) spread over all banks without padding.
+    // Chunk c of key row r sits at chunk slot c ^ swz(r) of its LDS row, so the
+    // operand reads below spread over all banks without padding.
     __shared__ __attribute__((aligned(16))) unsigned char klds[2][BN * ROW];
     __shared__ __attribute__((aligned(16))) unsigned char vlds[2][BN * ROW];
-    auto lds_off = [](int r, int byte) {  // byte offset of (row r, byte) in a tile
-        return r * ROW + ((((byte >> 4) ^ r) & (CPR - 1)) << 4) + (byte & 15);
-    };
 
     const size_t slot = (size_t)p.Hkv * D;
     const size_t rb = (size_t)row * p.C * slot + (size_t)kv * D;
@@ -281,19 +295,40 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     const uint32_t slotb = (uint32_t)(slot * 2);
 
     // tile t into buffer buf: wave w issues DMA instructions w, w + 4, ...; lane
-    // l of instruction i fetches chunk (l % CPR) ^ (r % CPR) of key row
+    // l of instruction i fetches chunk (l % CPR) ^ swz(r) of key row
     // r = RPI i + l / CPR (clamped into the prompt) into slot l % CPR
     auto load_tile = [&](int t, int buf) {
 #pragma unroll
         for (int i = w; i < NI; i += 4) {
             const int r = i * RPI + lane / CPR;
             const uint32_t off = (uint32_t)min(t * BN + r, nkeys - 1) * slotb +
-                                 ((((lane % CPR) ^ r) & (CPR - 1)) << 4);
+                                 ((((lane % CPR) ^ swz(r)) & (CPR - 1)) << 4);
             lds_dma16(kb + off, klds[buf] + i * 1024);
             lds_dma16(vb + off, vlds[buf] + i * 1024);
         }
     };
     load_tile(0, 0);
+
+    // Per-lane byte offsets of the operand reads inside a tile; the key block,
+    // the PV k-step and the buffer only add constants.
+    //   K: key row qi (+ 32 for the second block), chunk 2 ks + hh (dims
+    //      16 ks + 8 hh .. + 7);
+    //   V: key row 4 hh + j16 / 4 (+ 8 for the second read, + 16 / 32 for the
+    //      k-step), dims 32 db + 16 (g % 2) + 4 (j16 % 4) .. + 3.
+    const int j16 = lane & 15, g = lane >> 4;
+    uint32_t koff[KS], voff[2][NDB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        koff[ks] = qi * ROW + ((((2 * ks + hh) ^ swz(qi)) & (CPR - 1)) << 4);
+#pragma unroll
+    for (int s8 = 0; s8 < 2; ++s8) {
+        const int r = 4 * hh + (j16 >> 2) + 8 * s8;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = (32 * db + 16 * (g & 1) + 4 * (j16 & 3)) * 2;  // bytes
+            voff[s8][db] = r * ROW + ((((col >> 4) ^ swz(r)) & (CPR - 1)) << 4) + (col & 15);
+        }
+    }
 
     // B operands of QK: the rotated query of this lane's row, dims 16 ks + 8 hh + j
     bf16x8 bq[KS];
@@ -338,13 +373,16 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
         for (int i = 0; i < 16; ++i)
             O[db][i] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
+    bool fresh = true;  // no tile seen yet (wave-uniform)
+    const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
     __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA; the barrier covers the others
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        const bool more = t + 1 < ntiles;
-        if (more)
+    // one key tile from LDS buffer B (a compile-time constant, so every operand
+    // read is a per-lane offset plus an immediate)
+    auto tile = [&](const int t, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        if (t + 1 < ntiles)
             load_tile(t + 1, buf ^ 1);
         const int k0 = t * BN;
         // some key of the tile is visible to one of this wave's queries, and the
@@ -364,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                 u32x4 kf[2];
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
-                    kf[b] = *(const u32x4 *)(kt + lds_off(b * 32 + qi, (ks * 16 + hh * 8) * 2));
+                    kf[b] = *(const u32x4 *)(kt + koff[ks] + b * 32 * ROW);
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
                     st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[b]),
@@ -375,12 +413,14 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
             // query of the wave need the causal mask.
             float tmax = -INFINITY;
             if (k0 + BN - 1 > s0 + qw) {
+                // key k0 + 4 hh + rel is visible to query qrow iff rel <= lim
+                const int lim = s0 + qrow - k0 - 4 * hh;
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + b * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-                        st[b][i] = key <= s0 + qrow ? st[b][i] : -INFINITY;
+                        const int rel = b * 32 + 8 * (i >> 2) + (i & 3);
+                        st[b][i] = rel <= lim ? st[b][i] : -INFINITY;
                     }
             }
 #pragma unroll
@@ -390,7 +430,12 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                     tmax = fmaxf(tmax, st[b][i]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * p.scale_log2;
             const bool grow = tmax > m_run + HEADROOM;
-            if (__any(grow)) {
+            if (fresh) {
+                // the wave's first visible tile: key 0 is visible to every query,
+                // so every column's max is finite; O and l are still zero
+                m_run = tmax;
+                fresh = false;
+            } else if (__any(grow)) {
                 const float m_new = grow ? tmax : m_run;
                 const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                 l_run *= alpha;
@@ -409,23 +454,25 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                         __builtin_fmaf(st[k2 >> 1][8 * (k2 & 1) + 2 * e], p.scale_log2, -m_run));
                     const float p1 = __builtin_amdgcn_exp2f(
                         __builtin_fmaf(st[k2 >> 1][8 * (k2 & 1) + 2 * e + 1], p.scale_log2, -m_run));
-                    l_run += p0 + p1;
-                    v[e] = pack_bf16(p0, p1);
+                    const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+                    v[e] = __builtin_bit_cast(uint32_t, pk);
+                    // the row sum takes the same BF16 weights the PV product uses
+                    // (fed from the converted pair itself: reading the pair back
+                    // out of v[] compiled to the same register for every e)
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones2, l_run, false);
                 }
                 pb[k2] = __builtin_bit_cast(bf16x8, v);
             }
             // PV: slot j of k-step k2 is key 32 (k2 / 2) + 16 (k2 % 2) + 8 (j / 4) + 4 hh + j % 4
-            const int j16 = lane & 15, g = lane >> 4;
 #pragma unroll
             for (int k2 = 0; k2 < 4; ++k2) {
-                const int kbase = 32 * (k2 >> 1) + 16 * (k2 & 1) + 4 * hh + (j16 >> 2);
+                const int rows_k2 = (32 * (k2 >> 1) + 16 * (k2 & 1)) * ROW;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const int col = (32 * db + 16 * (g & 1) + 4 * (j16 & 3)) * 2;
                     const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(vt + lds_off(kbase, col)));
+                        (__attribute__((address_space(3))) s16x4 *)(vt + voff[0][db] + rows_k2));
                     const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(vt + lds_off(kbase + 8, col)));
+                        (__attribute__((address_space(3))) s16x4 *)(vt + voff[1][db] + rows_k2));
                     const s16x4 vv[2] = {v0, v1};
                     O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
                                                                     pb[k2], O[db], 0, 0, 0);
@@ -434,6 +481,11 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
         }
         __builtin_amdgcn_s_waitcnt(0);  // the next tile's DMA (this wave's share)
         __syncthreads();                // ... and every wave's; buffer buf is free again
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        tile(t, Buf<0>{});
+        if (t + 1 < ntiles)
+            tile(t + 1, Buf<1>{});
     }
 
     l_run += __shfl_xor(l_run, 32, 64);
@@ -444,9 +496,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                u32x2 v;
-                v[0] = f2bf(O[db][4 * r] * inv) | (f2bf(O[db][4 * r + 1] * inv) << 16);
-                v[1] = f2bf(O[db][4 * r + 2] * inv) | (f2bf(O[db][4 * r + 3] * inv) << 16);
+                u32x2 v;  // finite values: the conversion instruction rounds to nearest even
+                v[0] = pack_bf16(O[db][4 * r] * inv, O[db][4 * r + 1] * inv);
+                v[1] = pack_bf16(O[db][4 * r + 2] * inv, O[db][4 * r + 3] * inv);
                 *(u32x2 *)(out + 32 * db + 8 * r + 4 * hh) = v;
             }
     }
