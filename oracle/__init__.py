@@ -37,6 +37,10 @@ def bf16_to_f32(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
+# storage types of the 16-bit tensors (the oracle's ORC_BF16 / ORC_F16)
+DTYPES = {"bf16": 1, "f16": 2}
+
+
 class Oracle:
     """One loaded build of the oracle library (the default one, or a test mutant)."""
 
@@ -65,6 +69,16 @@ class Oracle:
         L.orc_prefill_chunk.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double] + [u16p] * 3 + \
             [i32p, i32p, i32p, u16p, u16p, u16p, i32p, ctypes.c_int]
         L.orc_prefill_chunk.restype = ctypes.c_int
+        L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_f16_to_f32.restype = ctypes.c_float
+        L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_decode_step_dt.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double] + [u16p] * 3 + \
+            [i32p, i32p, u16p, u16p, u16p, f32p]
+        L.orc_decode_step_dt.restype = ctypes.c_int
+        L.orc_prefill_chunk_dt.argtypes = [ctypes.c_int] * 8 + [ctypes.c_double] + [u16p] * 3 + \
+            [i32p, i32p, i32p, u16p, u16p, u16p, i32p, ctypes.c_int]
+        L.orc_prefill_chunk_dt.restype = ctypes.c_int
         self.L = L
         self.path = path
 
@@ -75,6 +89,13 @@ class Oracle:
 
     def bf16_to_f32(self, h):
         return float(self.L.orc_bf16_to_f32(int(h)))
+
+    def f32_to_f16(self, x):
+        """float32 scalar -> FP16 bits, through the oracle's own rounding."""
+        return int(self.L.orc_f32_to_f16(float(x)))
+
+    def f16_to_f32(self, h):
+        return float(self.L.orc_f16_to_f32(int(h)))
 
     # -- RoPE -------------------------------------------------------------------
     def rope_inv_freq(self, base, D):
@@ -101,8 +122,10 @@ class Oracle:
         return y
 
     # -- the path ---------------------------------------------------------------
-    def decode_step(self, q, k_new, v_new, positions, rows, Kc, Vc, base, want_f32=False):
+    def decode_step(self, q, k_new, v_new, positions, rows, Kc, Vc, base, want_f32=False,
+                    dtype="bf16"):
         """One decode step.  Kc and Vc ([S, C, Hkv, D] uint16) are updated IN PLACE.
+        dtype: "bf16" or "f16", the storage type the uint16 bit patterns hold.
 
         Returns out [A, Hq, D] uint16 (and the FP32 output before rounding if
         want_f32).  Raises OracleError on invalid arguments (nothing written).
@@ -121,7 +144,8 @@ class Oracle:
         assert positions.shape == (A,) and rows.shape == (A,)
         out = np.zeros((A, Hq, D), dtype=np.uint16)
         of = np.zeros((A, Hq, D), dtype=np.float32) if want_f32 else None
-        rc = self.L.orc_decode_step(A, S, C, Hq, Hkv, D, float(base), _p(q, ctypes.c_uint16),
+        rc = self.L.orc_decode_step_dt(DTYPES[dtype], A, S, C, Hq, Hkv, D, float(base),
+                                    _p(q, ctypes.c_uint16),
                                     _p(k_new, ctypes.c_uint16), _p(v_new, ctypes.c_uint16),
                                     _p(positions, ctypes.c_int32), _p(rows, ctypes.c_int32),
                                     _p(Kc, ctypes.c_uint16), _p(Vc, ctypes.c_uint16),
@@ -131,7 +155,7 @@ class Oracle:
         return (out, of) if want_f32 else out
 
     def prefill(self, q, k_new, v_new, rows, Kc, Vc, base, t_list=None, starts=None, lens=None,
-                out=None):
+                out=None, dtype="bf16"):
         """Equal-length prefill, or a chunk appended at per-entry starts.
         q [A,T,Hq,D], k_new/v_new [A,T,Hkv,D] (uint16); starts [A] (None = 0);
         lens [A] (None = T): entry a uses its first lens[a] tokens only.
@@ -154,7 +178,8 @@ class Oracle:
         tl = None if t_list is None else _c(t_list, np.int32)
         st = None if starts is None else _c(starts, np.int32)
         ln = None if lens is None else _c(lens, np.int32)
-        rc = self.L.orc_prefill_chunk(A, T, S, C, Hq, Hkv, D, float(base), _p(q, ctypes.c_uint16),
+        rc = self.L.orc_prefill_chunk_dt(DTYPES[dtype], A, T, S, C, Hq, Hkv, D, float(base),
+                                _p(q, ctypes.c_uint16),
                                 _p(k_new, ctypes.c_uint16), _p(v_new, ctypes.c_uint16),
                                 _p(st, ctypes.c_int32), _p(ln, ctypes.c_int32),
                                 _p(rows, ctypes.c_int32), _p(Kc, ctypes.c_uint16),

@@ -44,6 +44,9 @@
  *    together; the pages only define the start-0 case (empty rows).
  *  - A batch whose entries have different lengths is the separate
  *    equal-length groups the pages form, run one after another.
+ *  - FP16 storage (the pages' typed softmax covers FP16 and BF16) follows the
+ *    same steps with IEEE binary16 conversions: exact widening, and
+ *    round-to-nearest-even narrowing with subnormals and overflow to infinity.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
  * (see oracle/build.py).  -ffp-contract=off keeps every product rounded.
@@ -76,6 +79,71 @@ uint16_t orc_f32_to_bf16(float f)
     if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u)))
         keep += 1u; /* carries into the exponent correctly, up to infinity */
     return (uint16_t)keep;
+}
+
+/* ---------- FP16 <-> FP32 (IEEE 754 binary16) ----------------------------- */
+
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; exponent 0
+ * holds the subnormals frac * 2^-24, exponent 31 infinity and NaN. */
+float orc_f16_to_f32(uint16_t h)
+{
+    const int neg = h >> 15, ex = (h >> 10) & 31, fr = h & 1023;
+    if (ex == 31) {
+        uint32_t u = ((uint32_t)neg << 31) | 0x7f800000u | ((uint32_t)fr << 13);
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return f;
+    }
+    double v = ex == 0 ? ldexp((double)fr, -24) : ldexp((double)(1024 + fr), ex - 25);
+    return (float)(neg ? -v : v);
+}
+
+/* FP32 -> FP16, round to nearest, ties to even, through the subnormal range;
+ * magnitudes from 65520 (the midpoint above the largest finite 65504, which
+ * ties to the even neighbour 2^16) become infinity; NaN stays a quiet NaN. */
+uint16_t orc_f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)(sign | 0x7e00u | ((u >> 13) & 0x3ffu));
+    const double x = fabs((double)f);
+    if (x >= 65520.0)
+        return (uint16_t)(sign | 0x7c00u);
+    if (x == 0.0)
+        return sign;
+    int e;
+    frexp(x, &e);           /* x = m 2^e, 0.5 <= m < 1: binade of x is e - 1 */
+    int ex = e - 1;
+    if (ex < -14)
+        ex = -14;           /* subnormals share the quantum of the lowest binade */
+    const double n = x / ldexp(1.0, ex - 10);  /* x in quanta of its binade: exact */
+    double r = floor(n);
+    const double fr = n - r;
+    if (fr > 0.5 || (fr == 0.5 && fmod(r, 2.0) == 1.0))
+        r += 1.0;
+    if (r < 1024.0)         /* only in the lowest binade: a subnormal (or zero) */
+        return (uint16_t)(sign | (uint16_t)r);
+    if (r == 2048.0) {      /* rounded up into the next binade */
+        r = 1024.0;
+        ex += 1;
+    }
+    return (uint16_t)(sign | (uint16_t)((ex + 15) << 10) | (uint16_t)(r - 1024.0));
+}
+
+/* Storage types of the cache and the call's tensors. */
+#define ORC_BF16 1
+#define ORC_F16 2
+
+static float to_f32(int dt, uint16_t h)
+{
+    return dt == ORC_F16 ? orc_f16_to_f32(h) : orc_bf16_to_f32(h);
+}
+
+static uint16_t from_f32(int dt, float f)
+{
+    return dt == ORC_F16 ? orc_f32_to_f16(f) : orc_f32_to_bf16(f);
 }
 
 /* ---------- RoPE ---------------------------------------------------------- */
@@ -148,18 +216,18 @@ static int check_rows_unique(int A, int S, const int32_t *rows)
 /*
  * q_rot: rotated query (FP32, unrounded), D values.
  * Kr, Vr: the cache row base for kv head kv: element (j, d) at [j*row_stride + d].
- * out_bf16: D BF16 values.  e: scratch of last+1 floats.
+ * out_bits: D values of storage type dt.  e: scratch of last+1 floats.
  */
-static void attend_one(const float *q_rot, int D, const uint16_t *Kr, const uint16_t *Vr,
-                       long row_stride, int last, float scale, float *e, uint16_t *out_bf16,
-                       float *out_f32)
+static void attend_one(int dt, const float *q_rot, int D, const uint16_t *Kr,
+                       const uint16_t *Vr, long row_stride, int last, float scale, float *e,
+                       uint16_t *out_bits, float *out_f32)
 {
     float m = -INFINITY;
     for (int j = 0; j <= last; ++j) {
         const uint16_t *k = Kr + (long)j * row_stride;
         float dot = 0.0f;
         for (int d = 0; d < D; ++d)
-            dot = dot + q_rot[d] * orc_bf16_to_f32(k[d]);
+            dot = dot + q_rot[d] * to_f32(dt, k[d]);
         float sj = dot * scale;
         e[j] = sj;
         if (sj > m)
@@ -173,11 +241,11 @@ static void attend_one(const float *q_rot, int D, const uint16_t *Kr, const uint
     for (int d = 0; d < D; ++d) {
         float acc = 0.0f;
         for (int j = 0; j <= last; ++j)
-            acc = acc + e[j] * orc_bf16_to_f32(Vr[(long)j * row_stride + d]);
+            acc = acc + e[j] * to_f32(dt, Vr[(long)j * row_stride + d]);
         float o = acc / l;
         if (out_f32)
             out_f32[d] = o;
-        out_bf16[d] = orc_f32_to_bf16(o);
+        out_bits[d] = from_f32(dt, o);
     }
 }
 
@@ -186,18 +254,23 @@ static void attend_one(const float *q_rot, int D, const uint16_t *Kr, const uint
 /*
  * One layer of the positions-aware cached decode step.
  *
- *  q      [A, Hq, D]  BF16 bits      k_new, v_new [A, Hkv, D] BF16 bits
+ *  dt     storage type of every 16-bit tensor: ORC_BF16 or ORC_F16
+ *         (operator-development.md, "Public interfaces": typed FP16/BF16
+ *         softmax with FP32 reduction)
+ *  q      [A, Hq, D]  bits           k_new, v_new [A, Hkv, D] bits
  *  pos    [A] int32 in [0, C)        rows [A] int32 in [0, S), distinct
- *  Kc, Vc [S, C, Hkv, D] BF16 bits, updated in place (only (rows[a], pos[a]))
- *  out    [A, Hq, D] BF16 bits       out_f32: optional [A, Hq, D] FP32 before rounding
+ *  Kc, Vc [S, C, Hkv, D] bits, updated in place (only (rows[a], pos[a]))
+ *  out    [A, Hq, D] bits            out_f32: optional [A, Hq, D] FP32 before rounding
  *
  * Returns 0, or a nonzero code with nothing written when an argument is invalid.
  */
-int orc_decode_step(int A, int S, int C, int Hq, int Hkv, int D, double base,
-                    const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
-                    const int32_t *pos, const int32_t *rows, uint16_t *Kc, uint16_t *Vc,
-                    uint16_t *out, float *out_f32)
+int orc_decode_step_dt(int dt, int A, int S, int C, int Hq, int Hkv, int D, double base,
+                       const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                       const int32_t *pos, const int32_t *rows, uint16_t *Kc, uint16_t *Vc,
+                       uint16_t *out, float *out_f32)
 {
+    if (dt != ORC_BF16 && dt != ORC_F16)
+        return ORC_ERR_SHAPE;
     int rc = check_shapes(A, S, C, Hq, Hkv, D);
     if (rc)
         return rc;
@@ -238,10 +311,10 @@ int orc_decode_step(int A, int S, int C, int Hq, int Hkv, int D, double base,
             uint16_t *kd = Kc + rows[a] * row + (long)pos[a] * slot + (long)h * D;
             uint16_t *vd = Vc + rows[a] * row + (long)pos[a] * slot + (long)h * D;
             for (int d = 0; d < D; ++d)
-                x[d] = orc_bf16_to_f32(k[d]);
+                x[d] = to_f32(dt, k[d]);
             orc_rope_apply(x, D, cs, sn, y);
             for (int d = 0; d < D; ++d) {
-                kd[d] = orc_f32_to_bf16(y[d]);
+                kd[d] = from_f32(dt, y[d]);
                 vd[d] = v[d];
             }
         }
@@ -254,12 +327,12 @@ int orc_decode_step(int A, int S, int C, int Hq, int Hkv, int D, double base,
             int kv = hq / G;
             const uint16_t *qa = q + ((long)a * Hq + hq) * D;
             for (int d = 0; d < D; ++d)
-                x[d] = orc_bf16_to_f32(qa[d]);
+                x[d] = to_f32(dt, qa[d]);
             orc_rope_apply(x, D, cs, sn, y);
             const uint16_t *Kr = Kc + rows[a] * row + (long)kv * D;
             const uint16_t *Vr = Vc + rows[a] * row + (long)kv * D;
             long o = ((long)a * Hq + hq) * D;
-            attend_one(y, D, Kr, Vr, slot, pos[a], scale, e, out + o,
+            attend_one(dt, y, D, Kr, Vr, slot, pos[a], scale, e, out + o,
                        out_f32 ? out_f32 + o : NULL);
         }
     }
@@ -299,11 +372,14 @@ int orc_decode_step(int A, int S, int C, int Hq, int Hkv, int D, double base,
  * stored nor attended, and their output rows are not written.
  * t_list (optional) restricts which query positions t are computed.
  */
-int orc_prefill_chunk(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
-                      const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
-                      const int32_t *starts, const int32_t *lens, const int32_t *rows,
-                      uint16_t *Kc, uint16_t *Vc, uint16_t *out, const int32_t *t_list, int n_t)
+int orc_prefill_chunk_dt(int dt, int A, int T, int S, int C, int Hq, int Hkv, int D,
+                         double base, const uint16_t *q, const uint16_t *k_new,
+                         const uint16_t *v_new, const int32_t *starts, const int32_t *lens,
+                         const int32_t *rows, uint16_t *Kc, uint16_t *Vc, uint16_t *out,
+                         const int32_t *t_list, int n_t)
 {
+    if (dt != ORC_BF16 && dt != ORC_F16)
+        return ORC_ERR_SHAPE;
     int rc = check_shapes(A, S, C, Hq, Hkv, D);
     if (rc)
         return rc;
@@ -350,10 +426,10 @@ int orc_prefill_chunk(int A, int T, int S, int C, int Hq, int Hkv, int D, double
                 uint16_t *kd = Kc + rows[a] * row + (long)(s0 + t) * slot + (long)h * D;
                 uint16_t *vd = Vc + rows[a] * row + (long)(s0 + t) * slot + (long)h * D;
                 for (int d = 0; d < D; ++d)
-                    x[d] = orc_bf16_to_f32(k[d]);
+                    x[d] = to_f32(dt, k[d]);
                 orc_rope_apply(x, D, cs, sn, y);
                 for (int d = 0; d < D; ++d) {
-                    kd[d] = orc_f32_to_bf16(y[d]);
+                    kd[d] = from_f32(dt, y[d]);
                     vd[d] = v[d];
                 }
             }
@@ -373,17 +449,36 @@ int orc_prefill_chunk(int A, int T, int S, int C, int Hq, int Hkv, int D, double
                 int kv = hq / G;
                 const uint16_t *qa = q + (((long)a * T + t) * Hq + hq) * D;
                 for (int d = 0; d < D; ++d)
-                    x[d] = orc_bf16_to_f32(qa[d]);
+                    x[d] = to_f32(dt, qa[d]);
                 orc_rope_apply(x, D, cs, sn, y);
                 const uint16_t *Kr = Kc + rows[a] * row + (long)kv * D;
                 const uint16_t *Vr = Vc + rows[a] * row + (long)kv * D;
                 long o = (((long)a * T + t) * Hq + hq) * D;
-                attend_one(y, D, Kr, Vr, slot, s0 + t, scale, e, out + o, NULL);
+                attend_one(dt, y, D, Kr, Vr, slot, s0 + t, scale, e, out + o, NULL);
             }
         }
     }
     free(inv_freq); free(cs); free(sn); free(x); free(y); free(e);
     return ORC_OK;
+}
+
+/* The BF16 entry points. */
+int orc_decode_step(int A, int S, int C, int Hq, int Hkv, int D, double base,
+                    const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                    const int32_t *pos, const int32_t *rows, uint16_t *Kc, uint16_t *Vc,
+                    uint16_t *out, float *out_f32)
+{
+    return orc_decode_step_dt(ORC_BF16, A, S, C, Hq, Hkv, D, base, q, k_new, v_new, pos, rows,
+                              Kc, Vc, out, out_f32);
+}
+
+int orc_prefill_chunk(int A, int T, int S, int C, int Hq, int Hkv, int D, double base,
+                      const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                      const int32_t *starts, const int32_t *lens, const int32_t *rows,
+                      uint16_t *Kc, uint16_t *Vc, uint16_t *out, const int32_t *t_list, int n_t)
+{
+    return orc_prefill_chunk_dt(ORC_BF16, A, T, S, C, Hq, Hkv, D, base, q, k_new, v_new, starts,
+                                lens, rows, Kc, Vc, out, t_list, n_t);
 }
 
 /* Equal-length prefill into empty rows: the chunk at start 0 of every row. */

@@ -78,3 +78,24 @@ def rope_f64(x, pos, base):
     lo = x[..., :h] * c - x[..., h:] * s
     hi = x[..., h:] * c + x[..., :h] * s
     return np.concatenate([lo, hi], axis=-1)
+
+
+# ---- FP16 (IEEE binary16) codes: numpy's float16 is the library reference
+
+def f16_to_f32(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def f16_rne_f64_array(a):
+    """Round float64 values to FP16 codes (numpy's correctly rounded conversion)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(a, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def widen(bits, dtype):
+    """16-bit codes of storage type dtype ("bf16" / "f16") -> float32."""
+    return f16_to_f32(bits) if dtype == "f16" else to_f32(bits)
+
+
+def round_f64(a, dtype):
+    return f16_rne_f64_array(a) if dtype == "f16" else bf16_rne_f64_array(a)

@@ -16,8 +16,8 @@ import numpy as np
 import torch
 
 import workloads
-from bf16util import (bf16_exact, bf16_rne_f64, bf16_rne_f64_array, rope_f64, to_f32,
-                      ulp_dist)
+from bf16util import (bf16_exact, bf16_rne_f64, bf16_rne_f64_array, f16_rne_f64_array,
+                      f16_to_f32, rope_f64, to_f32, ulp_dist)
 from oracle import OracleError
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -561,11 +561,112 @@ def pin_chunk_errors(orc):
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------------------------------- FP16
+
+def pin_f16_rounding(orc):
+    """FP16 conversions: the hand values of tests/golden/f16_hand_values.txt
+    (binary16 definition), every one of the 65536 codes widened exactly as
+    numpy's float16 does, and random FP32 values over the whole FP16 range
+    (subnormals and overflow included) narrowed as numpy rounds them."""
+    with open(os.path.join(GOLDEN, "f16_hand_values.txt")) as f:
+        for line in f:
+            cols = line.split("#")[0].split()
+            if not cols:
+                continue
+            x = np.float32(float(cols[0]))
+            assert float(x) == float(cols[0]), cols[0]
+            assert orc.f32_to_f16(x) == int(cols[1], 16), cols
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = codes.view(np.float16).astype(np.float32)
+    got = np.array([orc.f16_to_f32(int(c)) for c in codes], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    rng = np.random.default_rng(6)
+    xs = (rng.uniform(-1.0, 1.0, 40000) * 2.0 ** rng.integers(-27, 18, 40000)).astype(np.float32)
+    # exact ties: codes' midpoints (from neighbouring FP16 values, exact in FP32)
+    lo = rng.integers(0, 0x7BFF, 4000).astype(np.uint16)
+    mid = ((lo.view(np.float16).astype(np.float64) +
+            (lo + 1).astype(np.uint16).view(np.float16).astype(np.float64)) / 2).astype(np.float32)
+    xs = np.concatenate([xs, mid, -mid, np.float32([np.inf, -np.inf])])
+    with np.errstate(over="ignore"):
+        want = xs.astype(np.float16).view(np.uint16)
+    got = np.array([orc.f32_to_f16(x) for x in xs], dtype=np.uint16)
+    assert np.array_equal(got, want)
+    q = orc.f32_to_f16(float("nan"))
+    assert (q & 0x7C00) == 0x7C00 and (q & 0x3FF) != 0
+
+
+def _f16_case(shape, rng, sigma=1.0):
+    return (rng.standard_normal(shape) * sigma).astype(np.float16).view(np.uint16)
+
+
+def pin_f16_decode_brute_force(orc):
+    """Decode with FP16 storage vs float64: K store within 1 FP16 ulp of the
+    float64 rotation, V bit-exact, output within 1 ulp of the float64 truth;
+    other rows untouched."""
+    A, S, C, Hq, Hkv, D, base = 3, 5, 40, 4, 2, 64, 1e4
+    G = Hq // Hkv
+    rng = np.random.default_rng(21)
+    q, k, v = _f16_case((A, Hq, D), rng), _f16_case((A, Hkv, D), rng), _f16_case((A, Hkv, D), rng)
+    K0, V0 = _f16_case((S, C, Hkv, D), rng), _f16_case((S, C, Hkv, D), rng)
+    pos = np.array([0, 17, 39], dtype=np.int32)
+    rows = np.array([4, 1, 2], dtype=np.int32)
+    Kc, Vc = K0.copy(), V0.copy()
+    out = orc.decode_step(q, k, v, pos, rows, Kc, Vc, base, dtype="f16")
+    touched = np.zeros((S, C), dtype=bool)
+    for a in range(A):
+        p_, r = int(pos[a]), int(rows[a])
+        touched[r, p_] = True
+        kref = f16_rne_f64_array(rope_f64(f16_to_f32(k[a]).astype(np.float64), p_, base))
+        assert ulp_dist(Kc[r, p_], kref).max() <= 1
+        assert np.array_equal(Vc[r, p_], v[a])
+        Kf = f16_to_f32(Kc[r, :p_ + 1]).astype(np.float64)
+        Vf = f16_to_f32(Vc[r, :p_ + 1]).astype(np.float64)
+        for hq in range(Hq):
+            qr = rope_f64(f16_to_f32(q[a, hq]).astype(np.float64), p_, base)
+            sc = Kf[:, hq // G] @ qr / math.sqrt(D)
+            w = np.exp(sc - sc.max())
+            o = (w @ Vf[:, hq // G]) / w.sum()
+            assert ulp_dist(out[a, hq], f16_rne_f64_array(o)).max() <= 1
+    assert np.array_equal(Kc[~touched], K0[~touched]) and np.array_equal(Vc[~touched], V0[~touched])
+
+
+def pin_f16_chunk_brute_force(orc):
+    """Prefill chunk with FP16 storage at two nonzero starts vs float64 causal
+    attention over the cached prefix and the chunk."""
+    A, T, S, C, Hq, Hkv, D, base = 2, 6, 3, 20, 4, 1, 32, 1e4
+    rng = np.random.default_rng(22)
+    q, k, v = (_f16_case((A, T, Hq, D), rng), _f16_case((A, T, Hkv, D), rng),
+               _f16_case((A, T, Hkv, D), rng))
+    K0, V0 = _f16_case((S, C, Hkv, D), rng), _f16_case((S, C, Hkv, D), rng)
+    rows = np.array([2, 0], dtype=np.int32)
+    starts = np.array([3, 14], dtype=np.int32)
+    Kc, Vc = K0.copy(), V0.copy()
+    out = orc.prefill(q, k, v, rows, Kc, Vc, base, starts=starts, dtype="f16")
+    for a in range(A):
+        r, s0 = int(rows[a]), int(starts[a])
+        for t in range(T):
+            kref = f16_rne_f64_array(rope_f64(f16_to_f32(k[a, t]).astype(np.float64), s0 + t, base))
+            assert ulp_dist(Kc[r, s0 + t], kref).max() <= 1
+        assert np.array_equal(Vc[r, s0:s0 + T], v[a])
+        Kf = f16_to_f32(Kc[r]).astype(np.float64)
+        Vf = f16_to_f32(Vc[r]).astype(np.float64)
+        for t in range(T):
+            for hq in range(Hq):
+                qr = rope_f64(f16_to_f32(q[a, t, hq]).astype(np.float64), s0 + t, base)
+                sc = Kf[:s0 + t + 1, 0] @ qr / math.sqrt(D)
+                w = np.exp(sc - sc.max())
+                o = (w @ Vf[:s0 + t + 1, 0]) / w.sum()
+                assert ulp_dist(out[a, t, hq], f16_rne_f64_array(o)).max() <= 1
+
+
 ALL_PINS = [
     pin_bf16_rounding, pin_rope_hand_values, pin_rope_identity_at_zero, pin_rope_norm,
     pin_rope_vs_f64, pin_rope_relative, pin_single_key, pin_uniform_softmax, pin_constant_v,
     pin_dominant_key, pin_brute_force_f64, pin_gqa_equals_mha, pin_untouched_and_sentinel,
     pin_idempotent_and_permutation, pin_errors, pin_prefill_brute_force,
     pin_decode_after_prefill, pin_prefill_subset, pin_chunk_brute_force,
-    pin_chunk_is_decode_steps, pin_ragged_groups, pin_chunk_errors,
+    pin_chunk_is_decode_steps, pin_ragged_groups, pin_chunk_errors, pin_f16_rounding,
+    pin_f16_decode_brute_force, pin_f16_chunk_brute_force,
 ]

@@ -5,7 +5,9 @@ library: a flipped rotation sign, a wrong RoPE frequency exponent, cycled
 instead of repeated GQA heads, a missing score scale, an exclusive causal
 bound, truncating BF16 rounding, a store into the wrong row, an unrotated
 query, a mirrored V store, a prefill chunk rotated, stored or attended as if
-it began at position 0.  Each must fail at least one pin.
+it began at position 0, FP16 conversions that truncate, round ties away,
+misplace the subnormal quantum or the overflow threshold, or read and store
+FP16 tensors as BF16.  Each must fail at least one pin.
 """
 import os
 
@@ -49,11 +51,20 @@ MUTANTS = [
      "orc_rope_cos_sin(t, D, inv_freq, cs, sn);\n            for (int h", 0),
     ("chunk_query_rotated_from_zero", "orc_rope_cos_sin(s0 + t, D, inv_freq, cs, sn);\n            for (int hq",
      "orc_rope_cos_sin(t, D, inv_freq, cs, sn);\n            for (int hq", 0),
-    ("chunk_keys_from_chunk_only", "attend_one(y, D, Kr, Vr, slot, s0 + t,",
-     "attend_one(y, D, Kr, Vr, slot, t,", 0),
+    ("chunk_keys_from_chunk_only", "attend_one(dt, y, D, Kr, Vr, slot, s0 + t,",
+     "attend_one(dt, y, D, Kr, Vr, slot, t,", 0),
     ("ragged_store_whole_chunk", "for (int t = 0; t < n; ++t) {\n            orc_rope_cos_sin",
      "for (int t = 0; t < T; ++t) {\n            orc_rope_cos_sin", 0),
     ("ragged_query_whole_chunk", "if (t >= n)\n                continue;", "", 0),
+    ("f16_truncating", "if (fr > 0.5 || (fr == 0.5 && fmod(r, 2.0) == 1.0))", "if (0)", 0),
+    ("f16_ties_away", "(fr == 0.5 && fmod(r, 2.0) == 1.0)", "(fr == 0.5)", 0),
+    ("f16_subnormal_quantum", "if (ex < -14)\n        ex = -14;", "if (ex < -15)\n        ex = -15;", 0),
+    ("f16_overflow_early", "if (x >= 65520.0)", "if (x >= 65504.0)", 0),
+    ("f16_widen_bias", "ldexp((double)(1024 + fr), ex - 25)", "ldexp((double)(1024 + fr), ex - 24)", 0),
+    ("f16_read_as_bf16", "return dt == ORC_F16 ? orc_f16_to_f32(h) : orc_bf16_to_f32(h);",
+     "return orc_bf16_to_f32(h);", 0),
+    ("f16_store_as_bf16", "return dt == ORC_F16 ? orc_f32_to_f16(f) : orc_f32_to_bf16(f);",
+     "return orc_f32_to_bf16(f);", 0),
     ("chunk_k_stored_from_zero", "uint16_t *kd = Kc + rows[a] * row + (long)(s0 + t) * slot",
      "uint16_t *kd = Kc + rows[a] * row + (long)t * slot", 0),
 ]
