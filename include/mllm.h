@@ -23,7 +23,9 @@
  *  - the compute calls never allocate, never synchronize and run only on the
  *    given stream.
  *
- * Layouts (all BF16, element strides, innermost dimension contiguous):
+ * Layouts (all in the cache's storage type, BF16 or FP16; element strides,
+ * innermost dimension contiguous).  rnd(x) below is x rounded to that type
+ * (nearest, ties to even):
  *  cache K, V : [slots, capacity, H_kv, D] per layer, dense
  *  decode  q  : [A, H_q, D]      k_new, v_new : [A, H_kv, D]    out : [A, H_q, D]
  *  prefill q  : [A, T, H_q, D]   k_new, v_new : [A, T, H_kv, D] out : [A, T, H_q, D]
@@ -52,7 +54,10 @@ typedef enum {
     MLLM_ERR_DEVICE = 8        /* a HIP runtime call failed; see mllm_last_error() */
 } mllm_status;
 
-typedef enum { MLLM_BF16 = 1 } mllm_dtype;
+/* Storage type of the cache and of every 16-bit tensor of a call (the typed
+ * FP16/BF16 softmax of operator-development.md, "Public interfaces"): one
+ * type per cache, and each view of a call must carry the cache's type. */
+typedef enum { MLLM_BF16 = 1, MLLM_F16 = 2 } mllm_dtype;
 
 /*
  * Non-owning tensor view ("Tensor ownership boundary": the C ABI builds a
@@ -79,7 +84,7 @@ typedef struct {
     int32_t capacity;  /* positions per row: the persistent bound on sequence length */
     int32_t h_kv;
     int32_t head_dim;  /* 64 or 128 */
-    int32_t dtype;     /* MLLM_BF16 */
+    int32_t dtype;     /* MLLM_BF16 or MLLM_F16 */
     int32_t device;
 } mllm_cache_desc;
 
@@ -130,7 +135,7 @@ mllm_status mllm_cache_alloc(const mllm_cache_desc *desc, mllm_cache **out);
 
 /* Wrap caller-owned device memory (e.g. torch tensors) as a cache.  k_layers
  * and v_layers hold num_layers pointers, each to a dense [slots, capacity,
- * h_kv, head_dim] BF16 block, 16-byte aligned.  The caller keeps ownership and
+ * h_kv, head_dim] block of desc->dtype, 16-byte aligned.  The caller keeps ownership and
  * must keep the memory alive until mllm_cache_free. */
 mllm_status mllm_cache_wrap(const mllm_cache_desc *desc, void *const *k_layers,
                             void *const *v_layers, mllm_cache **out);
@@ -168,10 +173,10 @@ mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32
  * positions[A] and cache_rows[A] parameterize decode RoPE, the K/V store and
  * cached attention; inactive rows untouched).  For every a < A, with
  * p = positions[a], r = cache_rows[a], on `stream`:
- *   1. K[r, p, h, :] = bf16(RoPE(k_new[a, h, :], p)) and V[r, p, h, :] =
+ *   1. K[r, p, h, :] = rnd(RoPE(k_new[a, h, :], p)) and V[r, p, h, :] =
  *      v_new[a, h, :] (bit copy) for every kv head h; no other cache byte is
  *      written;
- *   2. out[a, hq, :] = bf16( softmax_j( RoPE(q[a, hq], p) . K[r, j, hq/G] /
+ *   2. out[a, hq, :] = rnd( softmax_j( RoPE(q[a, hq], p) . K[r, j, hq/G] /
  *      sqrt(D) ) . V[r, j, hq/G] ) over j = 0..p, the softmax reduced in FP32
  *      and only the output rounded (operator-development.md, "Public
  *      interfaces": typed softmax reduces in FP32 registers).
@@ -224,11 +229,12 @@ mllm_status mllm_prefill_workspace_size(const mllm_cache *cache, int32_t A, int3
  * equal-length pending prompts run as one batch and each prefix is mapped
  * into its target empty shared-cache row; different lengths are separate
  * calls).  For every a < A and t < T, with r = cache_rows[a]:
- *   K[r, t, h, :] = bf16(RoPE(k_new[a, t, h, :], t)), V[r, t, h, :] = v_new[a, t, h, :];
+ *   K[r, t, h, :] = rnd(RoPE(k_new[a, t, h, :], t)), V[r, t, h, :] = v_new[a, t, h, :];
  *   out[a, t, hq, :] = causal GQA attention of RoPE(q[a, t, hq], t) over keys
- *   0..t of row r, FP32 softmax, BF16 output.  The attention products run on
- *   BF16 matrix cores: the rotated query and the softmax weights are rounded
- *   to BF16 before each product, accumulation is FP32.
+ *   0..t of row r, FP32 softmax, output rounded to the storage type.  The
+ *   attention products run on the matrix cores in the storage type: the
+ *   rotated query and the softmax weights are rounded to it before each
+ *   product, accumulation is FP32.
  * Positions >= T of row r and every other row stay untouched.
  *
  *  cache_rows_dev  : device int32[A]; cache_rows_host: host int32[A], the
@@ -259,11 +265,11 @@ mllm_status mllm_prefill_rope_store_attn(mllm_cache *cache, int32_t layer,
  * taken together, and a batch of several lengths as those equal-length groups
  * run one after another.  For every a < A, with s = starts[a],
  * n = lengths[a], r = rows[a], and every t < n:
- *   K[r, s+t, h, :] = bf16(RoPE(k_new[a, t, h, :], s+t)),
+ *   K[r, s+t, h, :] = rnd(RoPE(k_new[a, t, h, :], s+t)),
  *   V[r, s+t, h, :] = v_new[a, t, h, :];
  *   out[a, t, hq, :] = causal GQA attention of RoPE(q[a, t, hq], s+t) over
  *   keys 0..s+t of row r (the cached prefix and the chunk up to t), FP32
- *   softmax, BF16 output; the products run on BF16 matrix cores as in
+ *   softmax, rounded output; the products run on the matrix cores as in
  *   mllm_prefill_rope_store_attn.
  * Tokens t >= n of an entry are ignored and out[a, t] is not written; no
  * other cache byte is written.  starts 0 and lengths T on empty rows give

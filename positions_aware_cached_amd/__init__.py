@@ -18,6 +18,9 @@ OK = 0
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIAS", 4: "OUT_OF_RANGE",
           5: "ROW_BUSY", 6: "WORKSPACE", 7: "OUT_OF_MEMORY", 8: "DEVICE"}
 BF16 = 1
+F16 = 2
+# torch dtype -> storage type code of the C ABI
+DTYPE_CODES = {torch.bfloat16: BF16, torch.float16: F16}
 
 EXPORTS = ("mllm_abi_version", "mllm_last_error", "mllm_cache_bytes", "mllm_cache_alloc",
            "mllm_cache_wrap", "mllm_cache_free", "mllm_cache_layer", "mllm_cache_get_desc",
@@ -115,14 +118,14 @@ def view(t):
     v = TensorView()
     if t is None:
         return None
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"expected a bfloat16 tensor, got {t.dtype}")
+    if t.dtype not in DTYPE_CODES:
+        raise TypeError(f"expected a bfloat16 or float16 tensor, got {t.dtype}")
     if t.dim() > 4:
         raise ValueError("at most 4 dims")
     v.data = t.data_ptr() if t.numel() else (t.data_ptr() or None)
     v.bytes = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
     v.ndim = t.dim()
-    v.dtype = BF16
+    v.dtype = DTYPE_CODES[t.dtype]
     v.device = t.device.index if t.is_cuda else -1
     for i in range(t.dim()):
         v.shape[i] = t.shape[i]
@@ -149,8 +152,8 @@ def _opts(waves=0, kernel=0, attn_events=None):
     return o
 
 
-def cache_bytes(num_layers, slots, capacity, h_kv, head_dim, device=0):
-    d = CacheDesc(num_layers, slots, capacity, h_kv, head_dim, BF16, device)
+def cache_bytes(num_layers, slots, capacity, h_kv, head_dim, device=0, dtype=torch.bfloat16):
+    d = CacheDesc(num_layers, slots, capacity, h_kv, head_dim, DTYPE_CODES[dtype], device)
     n = ctypes.c_uint64()
     _check(load().mllm_cache_bytes(ctypes.byref(d), ctypes.byref(n)))
     return n.value
@@ -165,24 +168,27 @@ class Cache:
         self._keep = keep  # torch tensors that own wrapped memory
 
     @classmethod
-    def alloc(cls, num_layers, slots, capacity, h_kv, head_dim, device=0):
-        d = CacheDesc(num_layers, slots, capacity, h_kv, head_dim, BF16, device)
+    def alloc(cls, num_layers, slots, capacity, h_kv, head_dim, device=0, dtype=torch.bfloat16):
+        d = CacheDesc(num_layers, slots, capacity, h_kv, head_dim, DTYPE_CODES[dtype], device)
         h = ctypes.c_void_p()
         _check(load().mllm_cache_alloc(ctypes.byref(d), ctypes.byref(h)))
         return cls(h, d)
 
     @classmethod
     def wrap(cls, k_layers, v_layers):
-        """Wrap lists of [slots, capacity, h_kv, head_dim] bf16 CUDA tensors (one per layer)."""
+        """Wrap lists of [slots, capacity, h_kv, head_dim] CUDA tensors (one per layer), all
+        bfloat16 or all float16."""
         if len(k_layers) != len(v_layers) or not k_layers:
             raise ValueError("need the same positive number of K and V layers")
         t0 = k_layers[0]
         for t in list(k_layers) + list(v_layers):
-            if t.dtype != torch.bfloat16 or t.shape != t0.shape or not t.is_contiguous():
-                raise ValueError("every layer block must be a contiguous bf16 tensor of one shape")
+            if (t.dtype != t0.dtype or t.dtype not in DTYPE_CODES or t.shape != t0.shape
+                    or not t.is_contiguous()):
+                raise ValueError("every layer block must be a contiguous tensor of one shape and "
+                                 "one dtype (bfloat16 or float16)")
         S, C, Hkv, D = t0.shape
         dev = t0.device.index if t0.is_cuda else -1
-        d = CacheDesc(len(k_layers), S, C, Hkv, D, BF16, dev)
+        d = CacheDesc(len(k_layers), S, C, Hkv, D, DTYPE_CODES[t0.dtype], dev)
         n = len(k_layers)
         ks = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_layers])
         vs = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_layers])

@@ -13,49 +13,38 @@
 //   k_decode_merge    one wave per (entry, query head): rescales and sums the
 //                     partials of its segment (the streaming-attention merge
 //                     of the IPU refactor log, "Flash vs materialized
-//                     attention"), divides, rounds to BF16.
+//                     attention"), divides, rounds to the storage type.
 // Readable path (reference level, kept for diagnosis as the operator workflow
 // asks -- operator-development.md, "Acceptance rule"):
 //   k_rope_store      one block per entry: RoPE(K) + K/V store, rotated
 //                     queries in FP32 into the workspace;
 //   k_decode_readable one wave per (entry, query head), one key at a time.
 //
-// Numerics: the softmax runs in the log2 domain (scores pre-multiplied by
-// log2(e)/sqrt(D), exp2), every sum is FP32, only the output is rounded.
-// On the matrix cores the FP32 rotated query and the FP32 softmax weights
-// enter as sums of BF16 parts (see Cols below), so the products are those of
-// the FP32 values (exactly for up to 4 query heads per kv head, to 2^-16
-// relative beyond) and accumulate in FP32.
+// Every kernel is written once over the storage type E of the cache and the
+// tensors (BF16 or FP16, elem.h).  Numerics: the softmax runs in the log2
+// domain (scores pre-multiplied by log2(e)/sqrt(D), exp2), every sum is FP32,
+// only the output is rounded.  On the matrix cores the FP32 rotated query and
+// the FP32 softmax weights enter as sums of parts in the storage type (see
+// Cols below), so the products are those of the FP32 values (BF16: exactly
+// for up to 4 query heads per kv head, to 2^-16 relative beyond; FP16: to
+// 2^-22) and accumulate in FP32.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <mutex>
 
+#include "elem.h"
 #include "kernels.h"
 
 namespace mllm {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-// FP32 -> BF16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f2bf(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu))
-        return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 // Split-half rotation of one pair, every product and sum rounded separately
-// (contraction into fused multiply-adds is switched off: the BF16 rounding of
-// the result must see the same FP32 value as a separately rounded evaluation).
+// (contraction into fused multiply-adds is switched off: the rounding of the
+// result to the storage type must see the same FP32 value as a separately
+// rounded evaluation).
 __device__ __forceinline__ void rope_pair(float x, float y, float c, float s, float &lo, float &hi)
 {
 #pragma clang fp contract(off)
@@ -70,6 +59,7 @@ __device__ __forceinline__ bool entry_valid(const DecodeParams &p, int pos, int 
 }
 
 // ---------------------------------------------------------------- R1
+template <class E>
 __global__ __launch_bounds__(256) void k_rope_store(DecodeParams p)
 {
     const int a = blockIdx.x;
@@ -97,10 +87,10 @@ __global__ __launch_bounds__(256) void k_rope_store(DecodeParams p)
         const int h = idx / H, i = idx - h * H;
         const uint16_t *k = p.k_new + a * p.kn_sa + h * p.kn_sh;
         float lo, hi;
-        rope_pair(bf2f(k[i]), bf2f(k[i + H]), cs[i], sn[i], lo, hi);
+        rope_pair(E::to_f(k[i]), E::to_f(k[i + H]), cs[i], sn[i], lo, hi);
         uint16_t *kd = p.kc + dst + (size_t)h * D;
-        kd[i] = (uint16_t)f2bf(lo);
-        kd[i + H] = (uint16_t)f2bf(hi);
+        kd[i] = (uint16_t)E::from_f(lo);
+        kd[i + H] = (uint16_t)E::from_f(hi);
     }
     const int chunks = D / 8;
     for (int idx = t; idx < p.Hkv * chunks; idx += blockDim.x) {
@@ -112,7 +102,7 @@ __global__ __launch_bounds__(256) void k_rope_store(DecodeParams p)
         const int hq = idx / H, i = idx - hq * H;
         const uint16_t *q = p.q + a * p.q_sa + hq * p.q_sh;
         float lo, hi;
-        rope_pair(bf2f(q[i]), bf2f(q[i + H]), cs[i], sn[i], lo, hi);
+        rope_pair(E::to_f(q[i]), E::to_f(q[i + H]), cs[i], sn[i], lo, hi);
         float *qr = p.qrot + ((size_t)a * p.Hq + hq) * D;
         qr[i] = lo;
         qr[i + H] = hi;
@@ -128,7 +118,7 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-template <int D>
+template <class E, int D>
 __global__ __launch_bounds__(64) void k_decode_readable(DecodeParams p)
 {
     constexpr int PER = D / 64;
@@ -138,7 +128,7 @@ __global__ __launch_bounds__(64) void k_decode_readable(DecodeParams p)
     if (!entry_valid(p, pos, row)) {
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-            out[lane + 64 * e] = 0x7fc0;
+            out[lane + 64 * e] = E::qnan;
         return;
     }
     const int kv = hq / p.G;
@@ -157,7 +147,7 @@ __global__ __launch_bounds__(64) void k_decode_readable(DecodeParams p)
         float part = 0.0f;
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-            part += q[e] * bf2f(K[j * slot + lane + 64 * e]);
+            part += q[e] * E::to_f(K[j * slot + lane + 64 * e]);
         const float s = wave_sum(part) * p.scale_log2;
         const float mn = fmaxf(m, s);
         const float corr = exp2f(m - mn);
@@ -165,12 +155,12 @@ __global__ __launch_bounds__(64) void k_decode_readable(DecodeParams p)
         l = l * corr + pj;
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-            o[e] = o[e] * corr + pj * bf2f(V[j * slot + lane + 64 * e]);
+            o[e] = o[e] * corr + pj * E::to_f(V[j * slot + lane + 64 * e]);
         m = mn;
     }
 #pragma unroll
     for (int e = 0; e < PER; ++e)
-        out[lane + 64 * e] = (uint16_t)f2bf(o[e] / l);
+        out[lane + 64 * e] = (uint16_t)E::from_f(o[e] / l);
 }
 
 __device__ __forceinline__ float wave_max(float v)
@@ -206,25 +196,25 @@ __device__ __forceinline__ float wave_max(float v)
 //
 // Per 32-key tile: the next tile is in flight in registers (K in operand
 // order, V in row order, 16 B per lane) while this one is computed from LDS:
-//   QK  v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims of K, B = 32 dims x 16
-//       columns holding the BF16 parts of the FP32 rotated query heads; lane l
+//   QK  v_mfma_f32_16x16x32_{bf16,f16}: A = 16 keys x 32 dims of K, B = 32 dims
+//       x 16 columns holding the parts of the FP32 rotated query heads; lane l
 //       ends with the scores of keys 4 (l / 16) + i of column l % 16.
 //   softmax per column in FP32 (exp2 of log2(e)/sqrt(D)-scaled scores); the
 //       reference max moves only when a column max grows past a headroom, so
 //       the accumulators are rescaled rarely.
 //   PV  the same instruction with A = V^T read by ds_read_b64_tr_b16 from the
-//       row-major padded LDS tile and B = the BF16 parts of the FP32 weights.
+//       row-major padded LDS tile and B = the parts of the FP32 weights.
 //
-// Operand columns: part q (hi / mid / lo BF16 part) of head g sits in column
-// q GS + g (GCLS <= 8, one column group) or column g of group q (GCLS 16).
-// Three parts reproduce an FP32 value exactly (GCLS <= 4); two parts carry
-// it to 2^-16 relative (GCLS 8, 16).
+// Operand columns: part q (hi / mid / lo part, in the storage type) of head g
+// sits in column q GS + g (GCLS <= 8, one column group) or column g of group q
+// (GCLS 16).  BF16: three parts reproduce an FP32 value exactly (GCLS <= 4),
+// two carry it to 2^-16 relative (GCLS 8, 16); FP16: two parts, 2^-22.
 constexpr int kTile = 32;
 
-template <int GCLS>
+template <int GCLS, class E>
 struct Cols {
     static constexpr int GS = GCLS;
-    static constexpr int NPART = GCLS <= 4 ? 3 : 2;
+    static constexpr int NPART = GCLS <= 4 ? E::max_parts : 2;
     static constexpr int NGRP = GCLS == 16 ? 2 : 1;
 };
 
@@ -234,25 +224,6 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 // Its result for arguments below -126 is flushed to zero, which only drops
 // weights under 2^-126 of the running maximum.
 __device__ __forceinline__ float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// BF16 part `part` of x: with three parts hi + mid + lo == x exactly (each
-// remainder is exact and the last has at most 8 significant bits); with two
-// parts the remainder is rounded to nearest.
-template <int NPART>
-__device__ __forceinline__ uint32_t bf16_part(float x, int part)
-{
-    const uint32_t hi = __float_as_uint(x) & 0xffff0000u;
-    if (part == 0)
-        return hi >> 16;
-    const float r1 = x - __uint_as_float(hi);
-    if (NPART == 2)
-        return f2bf(r1);
-    const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
-    if (part == 1)
-        return mid >> 16;
-    const float r2 = r1 - __uint_as_float(mid);
-    return __float_as_uint(r2) >> 16;
-}
 
 // One 16-B global -> LDS load per active lane: lane l's bytes land at
 // lds_base + 16 l (the LDS base is wave-uniform).
@@ -387,10 +358,11 @@ constexpr int decode_lds_bytes(int hg)
 }
 
 // Up to 8 waves per group (2 per SIMD); 4 with 16-column operands (1 per SIMD).
-template <int D, int GCLS>
+template <class E, int D, int GCLS>
 __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(DecodeParams p)
 {
-    using CL = Cols<GCLS>;
+    using CL = Cols<GCLS, E>;
+    typedef typename E::vec8 vec8;
     constexpr int GS = CL::GS, NPART = CL::NPART, NGRP = CL::NGRP;
     constexpr int KS = D / 32;             // QK k-steps (32 dims each)
     constexpr int NDB = D / 16;            // PV dim blocks (16 dims each)
@@ -559,7 +531,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     // ---- per-segment state
     int nkeys = 0;
     bool owner = false;
-    bf16x8 bq[NGRP][KS];
+    vec8 bq[NGRP][KS];
     float m_run, l_run;
     f32x4 O[NGRP][NDB];
     auto start_segment = [&](int hg, int erow, int epos) {
@@ -572,8 +544,9 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             const size_t at = ((size_t)erow * p.C + epos) * slot + (size_t)eh * D;
             if (lane < D / 2) {
                 float lo, hi;
-                rope_pair(bf2f(kraw[lane]), bf2f(kraw[lane + D / 2]), cs[lane], sn[lane], lo, hi);
-                const uint16_t klo = (uint16_t)f2bf(lo), khi = (uint16_t)f2bf(hi);
+                rope_pair(E::to_f(kraw[lane]), E::to_f(kraw[lane + D / 2]), cs[lane], sn[lane], lo,
+                          hi);
+                const uint16_t klo = (uint16_t)E::from_f(lo), khi = (uint16_t)E::from_f(hi);
                 p.kc[at + lane] = klo;
                 p.kc[at + lane + D / 2] = khi;
                 newk[lane] = klo;
@@ -582,7 +555,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             if (lane < LPK)
                 *(u32x4 *)(p.vc + at + lane * 8) = *(const u32x4 *)(newv + lane * 8);
         }
-        // B operands of QK: BF16 parts of the rotated query, by column
+        // B operands of QK: the parts of the rotated query, by column
         float qv[KS][8];
         const unsigned char *qrow = (const unsigned char *)qlds + (ccol ? chead : 0) * D * 2;
 #pragma unroll
@@ -590,8 +563,8 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             const u32x4 v = *(const u32x4 *)(qrow + (ks * 32 + lg * 8) * 2);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                qv[ks][2 * e] = bf_lo(v[e]);
-                qv[ks][2 * e + 1] = bf_hi(v[e]);
+                qv[ks][2 * e] = E::lo(v[e]);
+                qv[ks][2 * e + 1] = E::hi(v[e]);
             }
         }
 #pragma unroll
@@ -612,11 +585,11 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
                 u32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t b0 = ccol ? bf16_part<NPART>(qv[ks][2 * e], part) : 0u;
-                    const uint32_t b1 = ccol ? bf16_part<NPART>(qv[ks][2 * e + 1], part) : 0u;
+                    const uint32_t b0 = ccol ? E::template part<NPART>(qv[ks][2 * e], part) : 0u;
+                    const uint32_t b1 = ccol ? E::template part<NPART>(qv[ks][2 * e + 1], part) : 0u;
                     v[e] = b0 | (b1 << 16);
                 }
-                bq[c][ks] = __builtin_bit_cast(bf16x8, v);
+                bq[c][ks] = __builtin_bit_cast(vec8, v);
             }
         }
         m_run = -INFINITY;
@@ -696,8 +669,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
                 const u32x4 kf = *(const u32x4 *)(klds + (b * KS + ks) * 1024 + lane * 16);
 #pragma unroll
                 for (int c = 0; c < NGRP; ++c)
-                    acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, kf), bq[c][ks], acc[b][c], 0, 0, 0);
+                    acc[b][c] = E::mma16(__builtin_bit_cast(vec8, kf), bq[c][ks], acc[b][c]);
             }
         float sc[NB][4];
         float tmax = -INFINITY;
@@ -742,7 +714,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             }
 
         // PV: k slot jj < 4 is key 4 lg + jj of block 0, slot 4 + jj of block 1
-        bf16x8 pb[NGRP];
+        vec8 pb[NGRP];
 #pragma unroll
         for (int c = 0; c < NGRP; ++c) {
             const int part = NGRP == 1 ? min(cpart, NPART - 1) : c;
@@ -750,9 +722,10 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int b = e >> 1, i = (e & 1) * 2;
-                v[e] = bf16_part<NPART>(pv[b][i], part) | (bf16_part<NPART>(pv[b][i + 1], part) << 16);
+                v[e] = E::template part<NPART>(pv[b][i], part) |
+                       (E::template part<NPART>(pv[b][i + 1], part) << 16);
             }
-            pb[c] = __builtin_bit_cast(bf16x8, v);
+            pb[c] = __builtin_bit_cast(vec8, v);
         }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -763,10 +736,10 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
                 (__attribute__((address_space(3))) s16x4 *)(vlds + (16 + lg * 4 + (n >> 2)) * VROW +
                                                             col));
             const s16x4 vv[2] = {v0, v1};
-            const bf16x8 vt = __builtin_bit_cast(bf16x8, vv);
+            const vec8 vt = __builtin_bit_cast(vec8, vv);
 #pragma unroll
             for (int c = 0; c < NGRP; ++c)
-                O[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb[c], O[c][db], 0, 0, 0);
+                O[c][db] = E::mma16(vt, pb[c], O[c][db]);
         }
         if (more && seg_ends)
             angles(nxa, nxpos);  // overlaps the loads in flight
@@ -799,10 +772,11 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
 // One wave per (entry, query head): the partials of segment (a, h = hq / G)
 // sit in slots seg + w for the waves w that touched it (the same plan as the
 // decode kernel); they are summed with weights 2^(m_w - M) (loads issued four
-// at a time), divided by the weighted sum of l_w and rounded to BF16.  An
+// at a time), divided by the weighted sum of l_w and rounded to the storage
+// type.  An
 // entry with an out-of-range position or row gets a NaN output and sets the
 // status word.
-template <int D>
+template <class E, int D>
 __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
 {
     constexpr int PER = D / 64;
@@ -812,7 +786,7 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
     if (!entry_valid(p, pos, row)) {
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-            out[lane + 64 * e] = 0x7fc0;
+            out[lane + 64 * e] = E::qnan;
         if (hq == 0 && lane == 0 && p.status)
             p.status[0] = 1;
         return;
@@ -870,7 +844,7 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
     const float L = wave_sum(lw);
 #pragma unroll
     for (int e = 0; e < PER; ++e)
-        out[lane + 64 * e] = (uint16_t)f2bf(O[e] / L);
+        out[lane + 64 * e] = (uint16_t)E::from_f(O[e] / L);
 }
 
 }  // namespace
@@ -891,11 +865,14 @@ DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t Hkv, int6
 
 hipError_t launch_rope_store(const DecodeParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL(k_rope_store, dim3(p.A), dim3(256), 0, stream, p);
+    if (p.dtype == F16::code)
+        hipLaunchKernelGGL(k_rope_store<F16>, dim3(p.A), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(k_rope_store<Bf16>, dim3(p.A), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, int GCLS>
+template <class E, int D, int GCLS>
 static hipError_t launch_stream_v(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
                                   hipEvent_t e1)
 {
@@ -903,46 +880,63 @@ static hipError_t launch_stream_v(const DecodeParams &p, hipStream_t stream, hip
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-        attr = hipFuncSetAttribute((const void *)k_decode_stream<D, GCLS>,
+        attr = hipFuncSetAttribute((const void *)k_decode_stream<E, D, GCLS>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                    decode_lds_bytes<D, GCLS>(GCLS == 16 ? 4 : 8));
     });
     if (attr != hipSuccess)
         return attr;
-    hipExtLaunchKernelGGL((k_decode_stream<D, GCLS>), dim3(p.NS), dim3(64 * p.HG), lds, stream, e0,
-                          e1, 0, p);
+    hipExtLaunchKernelGGL((k_decode_stream<E, D, GCLS>), dim3(p.NS), dim3(64 * p.HG), lds, stream,
+                          e0, e1, 0, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <class E, int D>
 static hipError_t launch_stream_d(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
                                   hipEvent_t e1)
 {
     if (p.G <= 1)
-        return launch_stream_v<D, 1>(p, stream, e0, e1);
+        return launch_stream_v<E, D, 1>(p, stream, e0, e1);
     if (p.G <= 2)
-        return launch_stream_v<D, 2>(p, stream, e0, e1);
+        return launch_stream_v<E, D, 2>(p, stream, e0, e1);
     if (p.G <= 4)
-        return launch_stream_v<D, 4>(p, stream, e0, e1);
+        return launch_stream_v<E, D, 4>(p, stream, e0, e1);
     if (p.G <= 8)
-        return launch_stream_v<D, 8>(p, stream, e0, e1);
-    return launch_stream_v<D, 16>(p, stream, e0, e1);
+        return launch_stream_v<E, D, 8>(p, stream, e0, e1);
+    return launch_stream_v<E, D, 16>(p, stream, e0, e1);
+}
+
+template <class E>
+static hipError_t launch_stream_e(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
+                                  hipEvent_t e1)
+{
+    return p.D == 64 ? launch_stream_d<E, 64>(p, stream, e0, e1)
+                     : launch_stream_d<E, 128>(p, stream, e0, e1);
 }
 
 hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
                                hipEvent_t e1)
 {
-    return p.D == 64 ? launch_stream_d<64>(p, stream, e0, e1)
-                     : launch_stream_d<128>(p, stream, e0, e1);
+    return p.dtype == F16::code ? launch_stream_e<F16>(p, stream, e0, e1)
+                                : launch_stream_e<Bf16>(p, stream, e0, e1);
+}
+
+template <class E>
+static void launch_merge_e(const DecodeParams &p, hipStream_t stream)
+{
+    const dim3 grid(p.Hq, p.A), block(64);
+    if (p.D == 64)
+        hipLaunchKernelGGL((k_decode_merge<E, 64>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((k_decode_merge<E, 128>), grid, block, 0, stream, p);
 }
 
 hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream)
 {
-    const dim3 grid(p.Hq, p.A), block(64);
-    if (p.D == 64)
-        hipLaunchKernelGGL(k_decode_merge<64>, grid, block, 0, stream, p);
+    if (p.dtype == F16::code)
+        launch_merge_e<F16>(p, stream);
     else
-        hipLaunchKernelGGL(k_decode_merge<128>, grid, block, 0, stream, p);
+        launch_merge_e<Bf16>(p, stream);
     return hipGetLastError();
 }
 
@@ -961,38 +955,53 @@ int decode_head_group(int Hkv, int G)
     return hg;
 }
 
-template <int D, int GCLS>
+template <class E, int D, int GCLS>
 static int resident_groups_v(int cus, int HG)
 {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_stream<D, GCLS>, 64 * HG,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_stream<E, D, GCLS>, 64 * HG,
                                                      decode_lds_bytes<D, GCLS>(HG)) != hipSuccess)
         return 0;
     return cus * per_cu;
 }
 
-int decode_resident_groups(int device, int D, int G, int HG)
+template <class E, int D>
+static int resident_groups_d(int cus, int G, int HG)
+{
+    return G <= 1 ? resident_groups_v<E, D, 1>(cus, HG)
+         : G <= 2 ? resident_groups_v<E, D, 2>(cus, HG)
+         : G <= 4 ? resident_groups_v<E, D, 4>(cus, HG)
+         : G <= 8 ? resident_groups_v<E, D, 8>(cus, HG)
+                  : resident_groups_v<E, D, 16>(cus, HG);
+}
+
+int decode_resident_groups(int device, int D, int G, int HG, int dtype)
 {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
         return 0;
-    if (D == 64)
-        return G <= 1 ? resident_groups_v<64, 1>(cus, HG) : G <= 2 ? resident_groups_v<64, 2>(cus, HG)
-             : G <= 4 ? resident_groups_v<64, 4>(cus, HG) : G <= 8 ? resident_groups_v<64, 8>(cus, HG)
-                      : resident_groups_v<64, 16>(cus, HG);
-    return G <= 1 ? resident_groups_v<128, 1>(cus, HG) : G <= 2 ? resident_groups_v<128, 2>(cus, HG)
-         : G <= 4 ? resident_groups_v<128, 4>(cus, HG) : G <= 8 ? resident_groups_v<128, 8>(cus, HG)
-                  : resident_groups_v<128, 16>(cus, HG);
+    if (dtype == F16::code)
+        return D == 64 ? resident_groups_d<F16, 64>(cus, G, HG) : resident_groups_d<F16, 128>(cus, G, HG);
+    return D == 64 ? resident_groups_d<Bf16, 64>(cus, G, HG) : resident_groups_d<Bf16, 128>(cus, G, HG);
+}
+
+template <class E>
+static void launch_readable_e(const DecodeParams &p, hipStream_t stream, hipEvent_t e0, hipEvent_t e1)
+{
+    const dim3 grid(p.Hq, p.A), block(64);
+    if (p.D == 64)
+        hipExtLaunchKernelGGL((k_decode_readable<E, 64>), grid, block, 0, stream, e0, e1, 0, p);
+    else
+        hipExtLaunchKernelGGL((k_decode_readable<E, 128>), grid, block, 0, stream, e0, e1, 0, p);
 }
 
 hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
                                   hipEvent_t e1)
 {
-    const dim3 grid(p.Hq, p.A), block(64);
-    if (p.D == 64)
-        hipExtLaunchKernelGGL(k_decode_readable<64>, grid, block, 0, stream, e0, e1, 0, p);
+    if (p.dtype == F16::code)
+        launch_readable_e<F16>(p, stream, e0, e1);
     else
-        hipExtLaunchKernelGGL(k_decode_readable<128>, grid, block, 0, stream, e0, e1, 0, p);
+        launch_readable_e<Bf16>(p, stream, e0, e1);
     return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ constexpr int kMaxHalfDim = 64;  // D / 2 for the largest supported head size (1
 
 // Everything one decode step needs, resolved and validated by the host layer.
 struct DecodeParams {
-    const uint16_t *q;      // [A, Hq, D] bf16, strides q_sa / q_sh (elements)
+    const uint16_t *q;      // [A, Hq, D] 16-bit codes, strides q_sa / q_sh (elements)
     const uint16_t *k_new;  // [A, Hkv, D]
     const uint16_t *v_new;  // [A, Hkv, D]
     int64_t q_sa, q_sh, kn_sa, kn_sh, vn_sa, vn_sh;
@@ -25,6 +25,7 @@ struct DecodeParams {
     float *part_o;    // workspace [slots, G, D]  per (segment, group, head) unnormalized outputs
     float *part_ml;   // workspace [slots, G, 2]  per (segment, group, head) (max, sum), log2 domain
     int32_t *status;  // optional device status word
+    int32_t dtype;     // storage type of every 16-bit tensor: 1 BF16, 2 FP16
     int32_t A, S, C, Hq, Hkv, D, G;
     int32_t NS;        // work groups of the decode launch
     int32_t HG, NHG;   // kv heads per group (one wave each), head groups per entry
@@ -48,8 +49,8 @@ hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEve
 // kv heads per work group for a head layout (a power of two dividing Hkv).
 int decode_head_group(int Hkv, int G);
 // Resident work groups of the decode kernel variant on a device (0 on error).
-int decode_resident_groups(int device, int D, int G, int HG);
-// Cross-wave merge -> BF16 output (one wave per entry and query head).
+int decode_resident_groups(int device, int D, int G, int HG, int dtype);
+// Cross-wave merge -> output in the storage type (one wave per entry and query head).
 hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream);
 // Readable one-wave-per-(entry, query head) attention straight to the output.
 hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream, hipEvent_t e0,
@@ -67,6 +68,7 @@ struct PrefillParams {
     uint16_t *out;          // [A, T, Hq, D]
     int64_t o_sa, o_st, o_sh;
     float2 *table;          // workspace [A, T, D/2] (cos, sin) of position starts[a] + t
+    int32_t dtype;          // storage type of every 16-bit tensor: 1 BF16, 2 FP16
     int32_t A, T, S, C, Hq, Hkv, D, G;
     float scale_log2;
     float inv_freq[kMaxHalfDim];

@@ -56,7 +56,7 @@ mllm_status hip_fail(hipError_t e, const char *what)
     return fail(MLLM_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int64_t kElem = 2;  // BF16 bytes
+constexpr int64_t kElem = 2;  // bytes of a BF16 or FP16 element
 
 mllm_status check_desc(const mllm_cache_desc *d)
 {
@@ -66,8 +66,8 @@ mllm_status check_desc(const mllm_cache_desc *d)
         return fail(MLLM_ERR_INVALID_ARG,
                     "num_layers, slots, capacity and h_kv must be positive (got %d %d %d %d)",
                     d->num_layers, d->slots, d->capacity, d->h_kv);
-    if (d->dtype != MLLM_BF16)
-        return fail(MLLM_ERR_UNSUPPORTED, "cache dtype %d unsupported (BF16 only)", d->dtype);
+    if (d->dtype != MLLM_BF16 && d->dtype != MLLM_F16)
+        return fail(MLLM_ERR_UNSUPPORTED, "cache dtype %d unsupported (BF16 or FP16)", d->dtype);
     if (d->head_dim != 64 && d->head_dim != 128)
         return fail(MLLM_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d->head_dim);
     if (d->device < 0)
@@ -107,16 +107,21 @@ mllm_status check_aliases(const std::vector<Range> &r)
     return MLLM_OK;
 }
 
-// Validate a BF16 view against an expected shape; returns its byte range.
+// Validate a view against an expected shape and the cache's dtype and
+// device; returns its byte range.
 mllm_status check_view(const mllm_tensor_view *v, const char *name, int ndim,
-                       const int64_t *shape, int device, bool writable, Range *range)
+                       const int64_t *shape, int device, int dtype, bool writable, Range *range)
 {
     if (!v)
         return fail(MLLM_ERR_INVALID_ARG, "%s view is null", name);
     if (v->ndim != ndim)
         return fail(MLLM_ERR_INVALID_ARG, "%s must have %d dims (got %d)", name, ndim, v->ndim);
-    if (v->dtype != MLLM_BF16)
-        return fail(MLLM_ERR_UNSUPPORTED, "%s dtype %d unsupported (BF16 only)", name, v->dtype);
+    if (v->dtype != MLLM_BF16 && v->dtype != MLLM_F16)
+        return fail(MLLM_ERR_UNSUPPORTED, "%s dtype %d unsupported (BF16 or FP16)", name,
+                    v->dtype);
+    if (v->dtype != dtype)
+        return fail(MLLM_ERR_INVALID_ARG, "%s dtype %d differs from the cache's %d", name,
+                    v->dtype, dtype);
     if (v->device != device)
         return fail(MLLM_ERR_INVALID_ARG, "%s is on device %d, cache on %d", name, v->device,
                     device);
@@ -196,19 +201,19 @@ mllm_status resolve_opts(const mllm_decode_opts *opts, int *waves, int *kernel)
 // Work groups of a decode launch (hg waves each, one per kv head of a head
 // group): the waves option divided by hg, else the device's resident groups
 // for the kernel variant (queried once per device and shape).
-int launch_groups(int requested_waves, int device, int D, int G, int hg)
+int launch_groups(int requested_waves, int device, int D, int G, int hg, int dtype)
 {
     if (requested_waves > 0)
         return std::max(1, requested_waves / hg);
     static std::mutex mu;
-    static std::map<std::tuple<int, int, int, int>, int> cache;
+    static std::map<std::tuple<int, int, int, int, int>, int> cache;
     const int gcls = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
     std::lock_guard<std::mutex> lock(mu);
-    auto key = std::make_tuple(device, D, gcls, hg);
+    auto key = std::make_tuple(device, D, gcls, hg, dtype);
     auto it = cache.find(key);
     if (it != cache.end())
         return it->second;
-    int ng = mllm::decode_resident_groups(device, D, G, hg);
+    int ng = mllm::decode_resident_groups(device, D, G, hg, dtype);
     if (ng <= 0)
         ng = 2048 / hg;
     ng = std::min(ng, MLLM_MAX_WAVES / hg);
@@ -441,10 +446,10 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
 
     Range rq, rk, rv, ro;
     const int64_t sq[3] = {A, Hq, D}, skv[3] = {A, d.h_kv, D};
-    if ((st = check_view(q, "q", 3, sq, d.device, false, &rq)) ||
-        (st = check_view(k_new, "k_new", 3, skv, d.device, false, &rk)) ||
-        (st = check_view(v_new, "v_new", 3, skv, d.device, false, &rv)) ||
-        (st = check_view(out, "out", 3, sq, d.device, true, &ro)))
+    if ((st = check_view(q, "q", 3, sq, d.device, d.dtype, false, &rq)) ||
+        (st = check_view(k_new, "k_new", 3, skv, d.device, d.dtype, false, &rk)) ||
+        (st = check_view(v_new, "v_new", 3, skv, d.device, d.dtype, false, &rv)) ||
+        (st = check_view(out, "out", 3, sq, d.device, d.dtype, true, &ro)))
         return st;
     if (A > 0 && (!positions_dev || !cache_rows_dev))
         return fail(MLLM_ERR_INVALID_ARG, "positions and cache_rows must be non-null");
@@ -525,7 +530,8 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     p.G = G;
     p.HG = mllm::decode_head_group(d.h_kv, G);
     p.NHG = d.h_kv / p.HG;
-    p.NS = launch_groups(waves, d.device, D, G, p.HG);
+    p.NS = launch_groups(waves, d.device, D, G, p.HG, d.dtype);
+    p.dtype = d.dtype;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     fill_inv_freq(p.inv_freq, rope->base, D);
 
@@ -614,10 +620,10 @@ mllm_status prefill_call(mllm_cache *cache, int32_t layer, const mllm_tensor_vie
         return st;
     Range rq, rk, rv, ro;
     const int64_t sq[4] = {A, T, Hq, D}, skv[4] = {A, T, d.h_kv, D};
-    if ((st = check_view(q, "q", 4, sq, d.device, false, &rq)) ||
-        (st = check_view(k_new, "k_new", 4, skv, d.device, false, &rk)) ||
-        (st = check_view(v_new, "v_new", 4, skv, d.device, false, &rv)) ||
-        (st = check_view(out, "out", 4, sq, d.device, true, &ro)))
+    if ((st = check_view(q, "q", 4, sq, d.device, d.dtype, false, &rq)) ||
+        (st = check_view(k_new, "k_new", 4, skv, d.device, d.dtype, false, &rk)) ||
+        (st = check_view(v_new, "v_new", 4, skv, d.device, d.dtype, false, &rv)) ||
+        (st = check_view(out, "out", 4, sq, d.device, d.dtype, true, &ro)))
         return st;
     if (chunk) {
         if (A > 0 && (!chunk_dev || !chunk_host))
@@ -710,6 +716,7 @@ mllm_status prefill_call(mllm_cache *cache, int32_t layer, const mllm_tensor_vie
     p.Hkv = d.h_kv;
     p.D = D;
     p.G = G;
+    p.dtype = d.dtype;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     fill_inv_freq(p.inv_freq, rope->base, D);
     hipEvent_t *ev = opts ? (hipEvent_t *)opts->attn_events : nullptr;

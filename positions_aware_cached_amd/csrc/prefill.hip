@@ -11,7 +11,7 @@
 // page's equal-length prefill into empty rows.
 //
 //   k_prefill_store     one block per (token t, entry a): split-half RoPE of
-//                       k_new -> BF16 store, v_new bit copy; the block also
+//                       k_new -> store in the storage type, v_new bit copy; the block also
 //                       writes the FP32 cos/sin table row of (a, t).
 //   k_prefill_mfma      the tuned attention: one workgroup of four waves per
 //                       (entry, query head, 128-query tile), FlashAttention-
@@ -23,6 +23,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include "elem.h"
 #include "kernels.h"
 
 namespace mllm {
@@ -31,10 +32,6 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // One 16-B global -> LDS load per active lane: lane l's bytes land at
 // lds_base + 16 l (the LDS base is wave-uniform).
@@ -44,26 +41,10 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds_base)
                                      (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
-// Two FP32 values -> packed BF16 (round to nearest even) with the gfx950
-// conversion instruction; used for matrix-core operands (finite values).
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
-
-__device__ __forceinline__ uint32_t f2bf(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu))
-        return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 // Split-half rotation of one pair, every product and sum rounded separately
-// (contraction into fused multiply-adds is switched off: the BF16 rounding of
-// the result must see the same FP32 value as a separately rounded evaluation).
+// (contraction into fused multiply-adds is switched off: the rounding of the
+// result to the storage type must see the same FP32 value as a separately
+// rounded evaluation).
 __device__ __forceinline__ void rope_pair(float x, float y, float c, float s, float &lo, float &hi)
 {
 #pragma clang fp contract(off)
@@ -90,6 +71,7 @@ __device__ __forceinline__ Chunk chunk_of(const PrefillParams &p, int a)
 
 // workspace: cos/sin table [A][T][D/2] of float2 (cos, sin), row (a, t) for
 // position s_a + t
+template <class E>
 __global__ __launch_bounds__(256) void k_prefill_store(PrefillParams p, float2 *table)
 {
     const int t = blockIdx.x, a = blockIdx.y, tid = threadIdx.x;
@@ -112,10 +94,10 @@ __global__ __launch_bounds__(256) void k_prefill_store(PrefillParams p, float2 *
         const int h = idx / H, i = idx - h * H;
         const uint16_t *k = p.k_new + a * p.kn_sa + t * p.kn_st + h * p.kn_sh;
         float lo, hi;
-        rope_pair(bf2f(k[i]), bf2f(k[i + H]), cs[i], sn[i], lo, hi);
+        rope_pair(E::to_f(k[i]), E::to_f(k[i + H]), cs[i], sn[i], lo, hi);
         uint16_t *kd = p.kc + dst + (size_t)h * D;
-        kd[i] = (uint16_t)f2bf(lo);
-        kd[i + H] = (uint16_t)f2bf(hi);
+        kd[i] = (uint16_t)E::from_f(lo);
+        kd[i + H] = (uint16_t)E::from_f(hi);
     }
     const int chunks = D / 8;
     for (int idx = tid; idx < p.Hkv * chunks; idx += blockDim.x) {
@@ -135,7 +117,7 @@ __device__ __forceinline__ float wave_sum(float v)
 
 // One wave per (a, t, hq).  Lane l owns dims l and l + 64 (D = 128) or l
 // (D = 64, the partner dim l +- 32 fetched by shuffle) of the query.
-template <int D>
+template <class E, int D>
 __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const float2 *table)
 {
     constexpr int H = D / 2;
@@ -145,7 +127,7 @@ __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const 
     if (!ch.ok) {  // device values disagree with the checked host copy: NaN output
 #pragma unroll
         for (int e = 0; e < D / 64; ++e)
-            out[lane + 64 * e] = 0x7fc0;
+            out[lane + 64 * e] = E::qnan;
         return;
     }
     if (t >= ch.n)
@@ -157,12 +139,12 @@ __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const 
     float q[D / 64];
     if (D == 128) {
         const float2 cs = tab[lane];
-        rope_pair(bf2f(qs[lane]), bf2f(qs[lane + 64]), cs.x, cs.y, q[0], q[D / 64 - 1]);
+        rope_pair(E::to_f(qs[lane]), E::to_f(qs[lane + 64]), cs.x, cs.y, q[0], q[D / 64 - 1]);
     } else {
         const int i = lane & (H - 1);
         const float2 cs = tab[i];
         float lo, hi;
-        rope_pair(bf2f(qs[i]), bf2f(qs[i + H]), cs.x, cs.y, lo, hi);
+        rope_pair(E::to_f(qs[i]), E::to_f(qs[i + H]), cs.x, cs.y, lo, hi);
         q[0] = lane < H ? lo : hi;
     }
     const size_t slot = (size_t)p.Hkv * D;
@@ -176,7 +158,7 @@ __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const 
         float part = 0.0f;
 #pragma unroll
         for (int e = 0; e < D / 64; ++e)
-            part += q[e] * bf2f(K[j * slot + lane + 64 * e]);
+            part += q[e] * E::to_f(K[j * slot + lane + 64 * e]);
         const float s = wave_sum(part) * p.scale_log2;
         const float mn = fmaxf(m, s);
         const float corr = exp2f(m - mn);
@@ -184,12 +166,12 @@ __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const 
         l = l * corr + pj;
 #pragma unroll
         for (int e = 0; e < D / 64; ++e)
-            o[e] = o[e] * corr + pj * bf2f(V[j * slot + lane + 64 * e]);
+            o[e] = o[e] * corr + pj * E::to_f(V[j * slot + lane + 64 * e]);
         m = mn;
     }
 #pragma unroll
     for (int e = 0; e < D / 64; ++e)
-        out[lane + 64 * e] = (uint16_t)f2bf(o[e] / l);
+        out[lane + 64 * e] = (uint16_t)E::from_f(o[e] / l);
 }
 
 
@@ -217,7 +199,7 @@ struct Buf {
 // query head hq, query tile q0 .. q0 + 127); the kv head is hq / G.  Key tiles
 // of 64 are staged through two padded LDS buffers (the next tile is loaded
 // into registers while the current one is computed).  Per tile and wave:
-//   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims of K, B =
+//   S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16} (A = 32 keys x 16 dims of K, B =
 //       16 dims x 32 queries of the rotated query): lane l owns query l % 32
 //       and keys 8 (i / 4) + 4 (l / 32) + i % 4 (i < 16) of each 32-key block,
 //       so the softmax over keys is in-lane plus one exchange with lane l ^ 32;
@@ -225,11 +207,14 @@ struct Buf {
 //   O^T += V^T P^T on the same instruction: the score registers are already
 //       the B operand (16 keys per k-step, in the key order above) and V^T is
 //       read from the row-major LDS tile with ds_read_b64_tr_b16 in that order.
-// The rotated query and the weights enter the matrix cores as BF16 (rounded
-// to nearest even); products accumulate in FP32; the output is rounded once.
-template <int D>
+// The rotated query and the weights enter the matrix cores in the storage
+// type (rounded to nearest even); products accumulate in FP32; the output is
+// rounded once.
+template <class E, int D>
 __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const float2 *table)
 {
+    typedef typename E::vec8 vec8;
+    typedef typename E::vec2 vec2;
     constexpr int BM = 128, BN = 64;
     constexpr int KS = D / 16;              // QK k-steps
     constexpr int NDB = D / 32;             // PV dim blocks
@@ -270,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     if (!ch.ok) {  // device values disagree with the checked host copy: NaN output
         if (qrow < p.T && hh == 0)
             for (int d = 0; d < D; ++d)
-                p.out[a * p.o_sa + qrow * p.o_st + hq * p.o_sh + d] = 0x7fc0;
+                p.out[a * p.o_sa + qrow * p.o_st + hq * p.o_sh + d] = E::qnan;
         return;
     }
     if (q0 >= ch.n)
@@ -331,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     }
 
     // B operands of QK: the rotated query of this lane's row, dims 16 ks + 8 hh + j
-    bf16x8 bq[KS];
+    vec8 bq[KS];
     {
         const int tq = min(qrow, n - 1);
         const uint16_t *qs = p.q + a * p.q_sa + tq * p.q_st + hq * p.q_sh;
@@ -341,8 +326,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
             const u32x4 v = *(const u32x4 *)(qs + ks * 16 + hh * 8);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[ks][2 * e] = __uint_as_float(v[e] << 16);
-                x[ks][2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+                x[ks][2 * e] = E::lo(v[e]);
+                x[ks][2 * e + 1] = E::hi(v[e]);
             }
         }
         const float2 *cs = table + ((size_t)a * p.T + tq) * (D / 2);
@@ -361,8 +346,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
             u32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                v[e] = pack_bf16(x[ks][2 * e], x[ks][2 * e + 1]);
-            bq[ks] = __builtin_bit_cast(bf16x8, v);
+                v[e] = E::pack2(x[ks][2 * e], x[ks][2 * e + 1]);
+            bq[ks] = __builtin_bit_cast(vec8, v);
         }
     }
 
@@ -374,7 +359,6 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
             O[db][i] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
     bool fresh = true;  // no tile seen yet (wave-uniform)
-    const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
     __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA; the barrier covers the others
     __syncthreads();
@@ -405,8 +389,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                     kf[b] = *(const u32x4 *)(kt + koff[ks] + b * 32 * ROW);
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
-                    st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[b]),
-                                                                    bq[ks], st[b], 0, 0, 0);
+                    st[b] = E::mma32(__builtin_bit_cast(vec8, kf[b]), bq[ks], st[b]);
             }
             // raw scores; the scale (> 0) is applied inside exp2 below, so the max
             // is taken on the raw values.  Only tiles that reach past the first
@@ -444,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                     O[db] *= alpha;
                 m_run = m_new;
             }
-            bf16x8 pb[4];
+            vec8 pb[4];
 #pragma unroll
             for (int k2 = 0; k2 < 4; ++k2) {
                 u32x4 v;
@@ -454,14 +437,14 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                         __builtin_fmaf(st[k2 >> 1][8 * (k2 & 1) + 2 * e], p.scale_log2, -m_run));
                     const float p1 = __builtin_amdgcn_exp2f(
                         __builtin_fmaf(st[k2 >> 1][8 * (k2 & 1) + 2 * e + 1], p.scale_log2, -m_run));
-                    const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+                    const vec2 pk = E::cvt2(p0, p1);
                     v[e] = __builtin_bit_cast(uint32_t, pk);
-                    // the row sum takes the same BF16 weights the PV product uses
+                    // the row sum takes the same rounded weights the PV product uses
                     // (fed from the converted pair itself: reading the pair back
                     // out of v[] compiled to the same register for every e)
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones2, l_run, false);
+                    l_run = E::sum2(pk, l_run);
                 }
-                pb[k2] = __builtin_bit_cast(bf16x8, v);
+                pb[k2] = __builtin_bit_cast(vec8, v);
             }
             // PV: slot j of k-step k2 is key 32 (k2 / 2) + 16 (k2 % 2) + 8 (j / 4) + 4 hh + j % 4
 #pragma unroll
@@ -474,8 +457,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                     const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) s16x4 *)(vt + voff[1][db] + rows_k2));
                     const s16x4 vv[2] = {v0, v1};
-                    O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                                    pb[k2], O[db], 0, 0, 0);
+                    O[db] = E::mma32(__builtin_bit_cast(vec8, vv), pb[k2], O[db]);
                 }
             }
         }
@@ -497,8 +479,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 u32x2 v;  // finite values: the conversion instruction rounds to nearest even
-                v[0] = pack_bf16(O[db][4 * r] * inv, O[db][4 * r + 1] * inv);
-                v[1] = pack_bf16(O[db][4 * r + 2] * inv, O[db][4 * r + 3] * inv);
+                v[0] = E::pack2(O[db][4 * r] * inv, O[db][4 * r + 1] * inv);
+                v[1] = E::pack2(O[db][4 * r + 2] * inv, O[db][4 * r + 3] * inv);
                 *(u32x2 *)(out + 32 * db + 8 * r + 4 * hh) = v;
             }
     }
@@ -512,31 +494,44 @@ uint64_t prefill_workspace_bytes(int64_t A, int64_t T, int64_t Hq, int64_t D)
     return ((uint64_t)A * T * (D / 2) * 8u + 255u) & ~uint64_t(255);
 }
 
-hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream, int kernel, hipEvent_t e0,
-                          hipEvent_t e1)
+template <class E>
+static void launch_prefill_e(const PrefillParams &p, hipStream_t stream, int kernel, hipEvent_t e0,
+                             hipEvent_t e1)
 {
-    float2 *table = p.table;
-    hipLaunchKernelGGL(k_prefill_store, dim3(p.T, p.A), dim3(256), 0, stream, p, table);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
+    const float2 *table = p.table;
     if (kernel == 1) {
         const dim3 grid(p.Hq, p.T, p.A);
         if (p.D == 64)
-            hipExtLaunchKernelGGL(k_prefill_readable<64>, grid, dim3(64), 0, stream, e0, e1, 0, p,
-                                  (const float2 *)table);
+            hipExtLaunchKernelGGL((k_prefill_readable<E, 64>), grid, dim3(64), 0, stream, e0, e1, 0,
+                                  p, table);
         else
-            hipExtLaunchKernelGGL(k_prefill_readable<128>, grid, dim3(64), 0, stream, e0, e1, 0, p,
-                                  (const float2 *)table);
+            hipExtLaunchKernelGGL((k_prefill_readable<E, 128>), grid, dim3(64), 0, stream, e0, e1, 0,
+                                  p, table);
     } else {
         const dim3 grid(p.Hq * p.A * ((p.T + 127) / 128));
         if (p.D == 64)
-            hipExtLaunchKernelGGL(k_prefill_mfma<64>, grid, dim3(256), 0, stream, e0, e1, 0, p,
-                                  (const float2 *)table);
+            hipExtLaunchKernelGGL((k_prefill_mfma<E, 64>), grid, dim3(256), 0, stream, e0, e1, 0, p,
+                                  table);
         else
-            hipExtLaunchKernelGGL(k_prefill_mfma<128>, grid, dim3(256), 0, stream, e0, e1, 0, p,
-                                  (const float2 *)table);
+            hipExtLaunchKernelGGL((k_prefill_mfma<E, 128>), grid, dim3(256), 0, stream, e0, e1, 0, p,
+                                  table);
     }
+}
+
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream, int kernel, hipEvent_t e0,
+                          hipEvent_t e1)
+{
+    if (p.dtype == F16::code)
+        hipLaunchKernelGGL(k_prefill_store<F16>, dim3(p.T, p.A), dim3(256), 0, stream, p, p.table);
+    else
+        hipLaunchKernelGGL(k_prefill_store<Bf16>, dim3(p.T, p.A), dim3(256), 0, stream, p, p.table);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    if (p.dtype == F16::code)
+        launch_prefill_e<F16>(p, stream, kernel, e0, e1);
+    else
+        launch_prefill_e<Bf16>(p, stream, kernel, e0, e1);
     return hipGetLastError();
 }
 

@@ -10,9 +10,9 @@ import torch
 import oracle
 import positions_aware_cached_amd as pac
 import workloads
-from bf16util import to_f32, ulp_dist
+from bf16util import ulp_dist, widen
 
-# Acceptance bar for the BF16 attention output (whole output tensor).
+# Acceptance bar for the attention output (whole output tensor), BF16 or FP16.
 MAX_ABS = 2e-2
 RMS = 4e-3
 
@@ -39,7 +39,8 @@ class DecodeRun:
         self.rows = torch.as_tensor(self.rows_h, device=dev)
         self.cache = pac.Cache.wrap([self.Kc], [self.Vc])
         A, Hq, D = self.q.shape
-        self.out = torch.empty((A, Hq, D), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((A, Hq, D), dtype=self.q.dtype, device=dev)
+        self.dtype = cfg.get("dtype", "bf16")
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def snapshot(self):
@@ -60,7 +61,7 @@ class DecodeRun:
         return self.out
 
 
-def oracle_rows(q, k_new, v_new, Kpre, Vpre, positions, rows, base, entries):
+def oracle_rows(q, k_new, v_new, Kpre, Vpre, positions, rows, base, entries, dtype="bf16"):
     """Run the oracle entry by entry on a host copy of each row's prefix.
 
     Returns {a: (out[Hq, D] uint16, k_slot[Hkv, D] uint16, v_slot[Hkv, D] uint16)}.
@@ -72,18 +73,20 @@ def oracle_rows(q, k_new, v_new, Kpre, Vpre, positions, rows, base, entries):
         p, r = int(positions[a]), int(rows[a])
         Km = workloads.bits(Kpre[r, :p + 1]).reshape((1, p + 1) + tuple(Kpre.shape[2:])).copy()
         Vm = workloads.bits(Vpre[r, :p + 1]).reshape((1, p + 1) + tuple(Vpre.shape[2:])).copy()
-        out = oracle.decode_step(qb[a:a + 1], kb[a:a + 1], vb[a:a + 1], [p], [0], Km, Vm, base)
+        out = oracle.decode_step(qb[a:a + 1], kb[a:a + 1], vb[a:a + 1], [p], [0], Km, Vm, base,
+                                 dtype=dtype)
         res[a] = (out[0], Km[0, p].copy(), Vm[0, p].copy())
     return res
 
 
-def check_output(got_bits, want_bits, what=""):
-    g = to_f32(got_bits).astype(np.float64)
-    w = to_f32(want_bits).astype(np.float64)
+def check_output(got_bits, want_bits, what="", dtype="bf16"):
+    g = widen(got_bits, dtype).astype(np.float64)
+    w = widen(want_bits, dtype).astype(np.float64)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     err = np.abs(g - w)
     mx, rms = float(err.max()), float(np.sqrt(np.mean(err ** 2)))
-    log(f"  {what}: max-abs {mx:.3e} rms {rms:.3e} exact {np.mean(got_bits == want_bits):.4f}")
+    log(f"  {what} ({dtype}): max-abs {mx:.3e} rms {rms:.3e} "
+        f"exact {np.mean(got_bits == want_bits):.4f}")
     assert mx <= MAX_ABS, f"{what}: max-abs {mx} > {MAX_ABS}"
     assert rms <= RMS, f"{what}: rms {rms} > {RMS}"
     return mx, rms
@@ -104,7 +107,7 @@ def full_parity(run, Kpre, Vpre, entries=None):
     A = run.q.shape[0]
     entries = range(A) if entries is None else entries
     want = oracle_rows(run.q, run.k_new, run.v_new, Kpre, Vpre, run.pos_h, run.rows_h,
-                       run.cfg["base"], entries)
+                       run.cfg["base"], entries, dtype=run.dtype)
     out = workloads.bits(run.out)
     got_o, want_o, kd = [], [], []
     for a, (o, ks, vs) in want.items():
@@ -119,7 +122,7 @@ def full_parity(run, Kpre, Vpre, entries=None):
         want_o.append(o)
     kd = np.concatenate([x.ravel() for x in kd])
     log(f"  K store: exact fraction {np.mean(kd == 0):.6f}, max ulp {kd.max()}")
-    return check_output(np.stack(got_o), np.stack(want_o), "output")
+    return check_output(np.stack(got_o), np.stack(want_o), "output", dtype=run.dtype)
 
 
 class _RawDevice:
@@ -141,7 +144,7 @@ def _loaded_hip_runtime():
 
 
 def copy_to_device_ptr(ptr, src, nbytes):
-    """Copy a host BF16 tensor into raw device memory (test plumbing only)."""
+    """Copy a host 16-bit tensor into raw device memory (test plumbing only)."""
     host = src.detach().contiguous().cpu().view(torch.int16).reshape(-1)
     assert host.numel() * 2 == nbytes
     try:

@@ -71,12 +71,12 @@ def fake_view(shape, addr=FAKE, strides=None, dtype=pac.BF16, device=0, nbytes=N
 class FakeCache:
     """A cache wrapping fake device addresses (wrap makes no HIP call)."""
 
-    def __init__(self, L=2, S=8, C=256, Hkv=2, D=64):
+    def __init__(self, L=2, S=8, C=256, Hkv=2, D=64, dtype=pac.BF16):
         self.S, self.C, self.Hkv, self.D = S, C, Hkv, D
         lb = S * C * Hkv * D * 2
         self.k = [FAKE + 0x100000000 * (2 * l + 1) for l in range(L)]
         self.v = [FAKE + 0x100000000 * (2 * l + 2) for l in range(L)]
-        d = pac.CacheDesc(L, S, C, Hkv, D, pac.BF16, 0)
+        d = pac.CacheDesc(L, S, C, Hkv, D, dtype, 0)
         ks = (ctypes.c_void_p * L)(*self.k)
         vs = (ctypes.c_void_p * L)(*self.v)
         h = ctypes.c_void_p()
@@ -283,3 +283,31 @@ def test_prefill_workspace_scales_with_entries():
     for A, T in [(1, 16), (3, 16), (16, 256)]:
         want = A * T * (fc.D // 2) * 8
         assert pac.prefill_workspace_size(fc.cache, A, T, 4) == (want + 255) // 256 * 256
+
+
+def test_dtype_rules():
+    """One storage type per cache (BF16 or FP16); every view of a call carries
+    the cache's type; unknown type codes are unsupported."""
+    fc = FakeCache(dtype=pac.F16)
+    D = fc.D
+    f16 = lambda shape, addr: fake_view(shape, addr, dtype=pac.F16)
+    q, k, v = f16([4, 4, D], FAKE + 0x1000000), f16([4, 2, D], FAKE + 0x2000000), \
+        f16([4, 2, D], FAKE + 0x3000000)
+    out = f16([4, 4, D], FAKE + 0x4000000)
+    # FP16 views on an FP16 cache pass the checks (the call then fails only at
+    # the device check: there is no GPU here)
+    st = call_decode(fc, q=q, k=k, v=v, out=out, mirror=[1, 2, 3, 4, 0, 1, 2, 3])
+    assert pac.STATUS[st] in ("DEVICE", "INVALID_ARG") and "dtype" not in pac.last_error()
+    expect(call_decode(fc, q=fake_view([4, 4, D], FAKE + 0x1000000), k=k, v=v, out=out),
+           "INVALID_ARG")                                           # BF16 q on an FP16 cache
+    expect(call_decode(fc, q=q, k=k, v=v, out=fake_view([4, 4, D], FAKE + 0x4000000)),
+           "INVALID_ARG")                                           # BF16 out
+    expect(call_decode(fc, q=fake_view([4, 4, D], FAKE + 0x1000000, dtype=3), k=k, v=v,
+                       out=out), "UNSUPPORTED")
+    d = pac.CacheDesc(1, 2, 16, 1, 64, 3, 0)
+    h = ctypes.c_void_p()
+    ks = (ctypes.c_void_p * 1)(FAKE)
+    vs = (ctypes.c_void_p * 1)(FAKE + 0x100000)
+    expect(pac.load().mllm_cache_wrap(ctypes.byref(d), ks, vs, ctypes.byref(h)), "UNSUPPORTED")
+    assert pac.cache_bytes(1, 2, 16, 1, 64, dtype=pac.torch.float16) == \
+        pac.cache_bytes(1, 2, 16, 1, 64)

@@ -45,7 +45,7 @@ class ChunkRun:
         self.cache = pac.Cache.wrap([self.Kc], [self.Vc])
         # raw bits: a NaN filled through a float value would be canonicalised
         self.out = torch.full(self.q.shape, int(SENT), dtype=torch.int16,
-                              device=device).view(torch.bfloat16)
+                              device=device).view(self.q.dtype)
 
     def run(self, kernel=0):
         A, T, Hq = self.q.shape[0], self.q.shape[1], self.q.shape[2]
@@ -73,7 +73,7 @@ def parity(run, Kpre, Vpre, entries=None, t_list=None):
         Vm = workloads.bits(Vpre[r:r + 1]).copy()
         ts = list(range(n)) if t_list is None else [t for t in t_list if t < n]
         o = oracle.prefill(qb[a:a + 1], kb[a:a + 1], vb[a:a + 1], [0], Km, Vm, run.cfg["base"],
-                           t_list=ts, starts=[s], lens=[n])
+                           t_list=ts, starts=[s], lens=[n], dtype=run.cfg["dtype"])
         vgot = workloads.bits(run.Vc[r, s:s + n])
         assert np.array_equal(vgot, Vm[0, s:s + n]), f"V store differs for entry {a}"
         d = ulp_dist(workloads.bits(run.Kc[r, s:s + n]), Km[0, s:s + n])
@@ -84,7 +84,7 @@ def parity(run, Kpre, Vpre, entries=None, t_list=None):
             got.append(out[a, t])
             want.append(o[0, t])
     H.log(f"  K store exact fraction {np.mean(np.concatenate(kd) == 0):.6f}")
-    return H.check_output(np.stack(got), np.stack(want), "chunk output")
+    return H.check_output(np.stack(got), np.stack(want), "chunk output", dtype=run.cfg["dtype"])
 
 
 def untouched(run, Kpre, Vpre):

@@ -63,7 +63,7 @@ def parity(run, Kpre, Vpre, entries=None, t_list=None):
         Km = workloads.bits(Kpre[r:r + 1]).copy()
         Vm = workloads.bits(Vpre[r:r + 1]).copy()
         o = oracle.prefill(qb[a:a + 1], kb[a:a + 1], vb[a:a + 1], [0], Km, Vm, run.cfg["base"],
-                           t_list=t_list)
+                           t_list=t_list, dtype=run.cfg["dtype"])
         kgot = workloads.bits(run.Kc[r, :T])
         vgot = workloads.bits(run.Vc[r, :T])
         assert np.array_equal(vgot, Vm[0, :T]), f"V store differs for entry {a}"
@@ -76,7 +76,8 @@ def parity(run, Kpre, Vpre, entries=None, t_list=None):
             want.append(o[0, t])
     kd = np.concatenate(kd)
     H.log(f"  K store exact fraction {np.mean(kd == 0):.6f}")
-    return H.check_output(np.stack(got), np.stack(want), "prefill output")
+    return H.check_output(np.stack(got), np.stack(want), "prefill output",
+                          dtype=run.cfg["dtype"])
 
 
 def untouched(run, Kpre, Vpre):

@@ -49,8 +49,14 @@ CONFIGS = {
 }
 
 
+# storage type of the 16-bit tensors: every config defaults to BF16; "f16"
+# draws the same N(0, sigma) values rounded to FP16 instead
+TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
 def config(name, **overrides):
     cfg = dict(CONFIGS[name])
+    cfg.setdefault("dtype", "bf16")
     cfg.update(overrides)
     cfg["name"] = name
     return cfg
@@ -103,9 +109,10 @@ def draw_chunk_meta(cfg):
     return starts.astype(np.int32), lens.astype(np.int32), rows.astype(np.int32)
 
 
-def _normal_bf16(shape, gen, device, sigma, chunk_elems=1 << 28):
-    """N(0, sigma) BF16 tensor drawn by torch (drawn in chunks along dim 0)."""
-    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+def _normal(shape, gen, device, sigma, dtype="bf16", chunk_elems=1 << 28):
+    """N(0, sigma) tensor drawn by torch in FP32 and rounded to the storage
+    type (drawn in chunks along dim 0)."""
+    out = torch.empty(shape, dtype=TORCH_DTYPES[dtype], device=device)
     flat = out.view(shape[0], -1)
     per = max(1, chunk_elems // max(1, flat.shape[1]))
     for i in range(0, shape[0], per):
@@ -130,18 +137,18 @@ def draw_decode(cfg, device="cpu"):
     pos, rows = draw_indices(cfg)
     gen = torch.Generator(device=device)
     gen.manual_seed(1000 + cfg["seed"])
-    q = _normal_bf16((A, Hq, D), gen, device, sigma)
-    k_new = _normal_bf16((A, Hkv, D), gen, device, sigma)
-    v_new = _normal_bf16((A, Hkv, D), gen, device, sigma)
-    Kc = _normal_bf16((S, C, Hkv, D), gen, device, sigma)
-    Vc = _normal_bf16((S, C, Hkv, D), gen, device, sigma)
+    q = _normal((A, Hq, D), gen, device, sigma, cfg["dtype"])
+    k_new = _normal((A, Hkv, D), gen, device, sigma, cfg["dtype"])
+    v_new = _normal((A, Hkv, D), gen, device, sigma, cfg["dtype"])
+    Kc = _normal((S, C, Hkv, D), gen, device, sigma, cfg["dtype"])
+    Vc = _normal((S, C, Hkv, D), gen, device, sigma, cfg["dtype"])
     if cfg.get("inactive") == "sentinel":
         inactive = np.setdiff1d(np.arange(S), rows)
         if inactive.size:
             idx = torch.as_tensor(inactive, device=device, dtype=torch.long)
-            sent = torch.tensor(NAN_SENTINEL, dtype=torch.int16).view(torch.bfloat16).item()
-            Kc.index_fill_(0, idx, sent)
-            Vc.index_fill_(0, idx, sent)
+            sent = torch.tensor(NAN_SENTINEL, dtype=torch.int16)
+            Kc.view(torch.int16).index_fill_(0, idx, sent)
+            Vc.view(torch.int16).index_fill_(0, idx, sent)
     return dict(q=q, k_new=k_new, v_new=v_new, Kc=Kc, Vc=Vc, positions=pos, rows=rows)
 
 
@@ -157,15 +164,15 @@ def draw_cache_layers(cfg, layers, device="cuda"):
     for l in range(layers):
         gen = torch.Generator(device=device)
         gen.manual_seed(5000 + 97 * cfg["seed"] + l)
-        Kc = _normal_bf16((S, C, Hkv, D), gen, device, sigma)
-        Vc = _normal_bf16((S, C, Hkv, D), gen, device, sigma)
+        Kc = _normal((S, C, Hkv, D), gen, device, sigma, cfg["dtype"])
+        Vc = _normal((S, C, Hkv, D), gen, device, sigma, cfg["dtype"])
         if cfg.get("inactive") == "sentinel":
             inactive = np.setdiff1d(np.arange(S), rows)
             if inactive.size:
                 idx = torch.as_tensor(inactive, device=device, dtype=torch.long)
-                sent = torch.tensor(NAN_SENTINEL, dtype=torch.int16).view(torch.bfloat16).item()
-                Kc.index_fill_(0, idx, sent)
-                Vc.index_fill_(0, idx, sent)
+                sent = torch.tensor(NAN_SENTINEL, dtype=torch.int16)
+                Kc.view(torch.int16).index_fill_(0, idx, sent)
+                Vc.view(torch.int16).index_fill_(0, idx, sent)
         out.append((Kc, Vc))
     return out
 
@@ -182,16 +189,16 @@ def draw_prefill(cfg, device="cpu"):
         _, rows = draw_indices(cfg)
     gen = torch.Generator(device=device)
     gen.manual_seed(2000 + cfg["seed"])
-    q = _normal_bf16((A, T, Hq, D), gen, device, sigma)
-    k_new = _normal_bf16((A, T, Hkv, D), gen, device, sigma)
-    v_new = _normal_bf16((A, T, Hkv, D), gen, device, sigma)
-    Kc = _normal_bf16((S, C, Hkv, D), gen, device, sigma)
-    Vc = _normal_bf16((S, C, Hkv, D), gen, device, sigma)
+    q = _normal((A, T, Hq, D), gen, device, sigma, cfg["dtype"])
+    k_new = _normal((A, T, Hkv, D), gen, device, sigma, cfg["dtype"])
+    v_new = _normal((A, T, Hkv, D), gen, device, sigma, cfg["dtype"])
+    Kc = _normal((S, C, Hkv, D), gen, device, sigma, cfg["dtype"])
+    Vc = _normal((S, C, Hkv, D), gen, device, sigma, cfg["dtype"])
     return dict(q=q, k_new=k_new, v_new=v_new, Kc=Kc, Vc=Vc, rows=rows)
 
 
 def bits(t):
-    """BF16 torch tensor -> numpy uint16 bit patterns (a host copy)."""
+    """16-bit torch tensor (BF16 or FP16) -> numpy uint16 bit patterns (a host copy)."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
