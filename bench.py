@@ -50,6 +50,10 @@ def parse():
                     help="also time the equal-length batched prefill (0 = skip)")
     ap.add_argument("--chunk-steps", type=int, default=20,
                     help="also time the prefill chunk of mixed starts and lengths (0 = skip)")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
+                    help="storage type of the cache and tensors of the headline run")
+    ap.add_argument("--f16-steps", type=int, default=50,
+                    help="also time the decode step and the prefill with FP16 storage (0 = skip)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times): the reference that "
                          "scales the HBM byte counters of a profiler run")
@@ -141,17 +145,97 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = workloads.config(args.workload)
+    hip = hip_runtime()
+    d = decode_leg(args, hip, args.dtype, args.steps, args.warmup, args.layers)
+    cfg, inp, cache, pos, rows, out, ws, mirror, call = (d[k] for k in (
+        "cfg", "inp", "cache", "pos", "rows", "out", "ws", "mirror", "call"))
     A, S, C, Hq, Hkv, D = (cfg[k] for k in ("A", "S", "C", "Hq", "Hkv", "D"))
-    print(f"[bench] drawing {args.workload} inputs + {args.layers} layer caches", file=sys.stderr,
+    pos_h, rows_h, ctx = d["pos_h"], d["rows_h"], d["ctx"]
+    kv_bytes, total_bytes, wall, attn_ms, step_ms = (d[k] for k in (
+        "kv_bytes", "total_bytes", "wall", "attn_ms", "step_ms"))
+    K, W, L = args.steps, args.warmup, args.layers
+    ms_per_step = wall * 1e3 / K
+    kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    tot_gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
+    attn_avg = float(np.mean(attn_ms))
+    attn_gbs = kv_bytes / (attn_avg * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}_decode", "A": A, "slots": S, "capacity": C,
+                   "h_q": Hq, "h_kv": Hkv, "head_dim": D, "rope_base": cfg["base"],
+                   "ctx_mean": round(float(ctx.mean()), 1), "ctx_max": int(ctx.max()),
+                   "layers_rotated": L, "waves": args.waves or "resident",
+                   "kernel": "fused stream" if args.kernel == 0 else "readable"},
+        "pct_hbm_peak": round(100.0 * tot_gbs / PEAK_HBM_GBS, 2),
+        "total_gbs": round(tot_gbs, 1),
+        "tokens_per_s": round(A / (ms_per_step * 1e-3), 1),
+        "step_ms_median": round(percentile(step_ms, 50), 4),
+        "step_ms_p95": round(percentile(step_ms, 95), 4),
+        "kv_bytes_per_step": kv_bytes,
+        "total_bytes_per_step": total_bytes,
+        "roofline": {
+            "kernel": "k_decode_stream" if args.kernel == 0 else "k_decode_readable",
+            "bound": "hbm",
+            "achieved": round(attn_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic("k_decode_stream" if args.kernel == 0 else
+                                        "k_decode_readable", f"{args.workload}_decode"
+                                        + ("_f16" if args.dtype == "f16" else "")),
+            "avg_launch_ms": round(attn_avg, 5),
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+
+    if args.graph_reps > 0:
+        res["graph"] = bench_graph(args, cache, inp, pos, rows, out, ws, mirror, cfg, kv_bytes)
+    if args.prefill_steps > 0:
+        res["prefill"] = bench_prefill(args, hip, "prefill", args.prefill_steps)
+    if args.chunk_steps > 0:
+        res["chunk"] = bench_prefill(args, hip, "chunk", args.chunk_steps)
+    if args.f16_steps > 0 and args.dtype != "f16":
+        res["f16"] = bench_f16(args, hip)
+    if args.cpu_seconds > 0:
+        call(0)  # a fresh layer-0 step: the oracle sample is compared with it
+        torch.cuda.synchronize()
+        res["cpu_baseline"] = cpu_baseline(args, cfg, inp, d["layers"], pos_h, rows_h, out)
+    print(json.dumps(res), flush=True)
+
+
+def decode_leg(args, hip, dtype, K, W, L):
+    """The decode step on the --workload configuration with storage type dtype:
+    W warm-up and K timed steps rotating over L layer caches; the attention
+    kernel's own duration from events stamped in its dispatch."""
+    import torch
+
+    import positions_aware_cached_amd as pac
+    import workloads
+
+    dev = torch.device("cuda:0")
+    cfg = workloads.config(args.workload, dtype=dtype)
+    A, S, C, Hq, Hkv, D = (cfg[k] for k in ("A", "S", "C", "Hq", "Hkv", "D"))
+    print(f"[bench] drawing {args.workload} {dtype} inputs + {L} layer caches", file=sys.stderr,
           flush=True)
     inp = workloads.draw_decode(cfg, device="cuda")
-    layers = [(inp["Kc"], inp["Vc"])] + workloads.draw_cache_layers(cfg, args.layers - 1)
+    layers = [(inp["Kc"], inp["Vc"])] + workloads.draw_cache_layers(cfg, L - 1)
     cache = pac.Cache.wrap([k for k, _ in layers], [v for _, v in layers])
     pos_h, rows_h = inp["positions"], inp["rows"]
     pos = torch.as_tensor(pos_h, device=dev)
     rows = torch.as_tensor(rows_h, device=dev)
-    out = torch.empty((A, Hq, D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((A, Hq, D), dtype=inp["q"].dtype, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     mirror = np.concatenate([pos_h, rows_h]).astype(np.int32)
     nws = pac.decode_workspace_size(cache, A, Hq, int(pos_h.max()), args.waves,
@@ -167,8 +251,6 @@ def main():
     io_bytes = A * Hq * D * 2 * 2 + 2 * A * Hkv * D * 2 * 2 + 8 * A
     total_bytes = kv_bytes + io_bytes
 
-    hip = hip_runtime()
-    K, W, L = args.steps, args.warmup, args.layers
     evs = []
     for _ in range(K):
         pair = (ctypes.c_void_p * 2)()
@@ -211,62 +293,31 @@ def main():
     torch.cuda.synchronize()
     step_ms = [a.elapsed_time(b) for a, b in step_ev]
 
-    ms_per_step = wall * 1e3 / K
-    kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    tot_gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
-    attn_avg = float(np.mean(attn_ms))
-    attn_gbs = kv_bytes / (attn_avg * 1e-3) / 1e9
+    return dict(cfg=cfg, inp=inp, cache=cache, pos=pos, rows=rows, out=out, ws=ws, mirror=mirror,
+                call=call, status=status, layers=layers, pos_h=pos_h, rows_h=rows_h, ctx=ctx, kv_bytes=kv_bytes,
+                total_bytes=total_bytes, wall=wall, attn_ms=attn_ms, step_ms=step_ms)
 
-    res = {
-        "metric": METRIC,
-        "value": round(kv_gbs, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{args.workload}_decode", "A": A, "slots": S, "capacity": C,
-                   "h_q": Hq, "h_kv": Hkv, "head_dim": D, "rope_base": cfg["base"],
-                   "ctx_mean": round(float(ctx.mean()), 1), "ctx_max": int(ctx.max()),
-                   "layers_rotated": L, "waves": args.waves or "resident",
-                   "kernel": "fused stream" if args.kernel == 0 else "readable"},
-        "pct_hbm_peak": round(100.0 * tot_gbs / PEAK_HBM_GBS, 2),
-        "total_gbs": round(tot_gbs, 1),
-        "tokens_per_s": round(A / (ms_per_step * 1e-3), 1),
-        "step_ms_median": round(percentile(step_ms, 50), 4),
-        "step_ms_p95": round(percentile(step_ms, 95), 4),
-        "kv_bytes_per_step": kv_bytes,
-        "total_bytes_per_step": total_bytes,
-        "roofline": {
-            "kernel": "k_decode_stream" if args.kernel == 0 else "k_decode_readable",
-            "bound": "hbm",
-            "achieved": round(attn_gbs, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic("k_decode_stream" if args.kernel == 0 else
-                                        "k_decode_readable", f"{args.workload}_decode"),
-            "avg_launch_ms": round(attn_avg, 5),
-            "algorithmic_bytes_per_launch": kv_bytes,
-        },
-    }
 
-    if args.graph_reps > 0:
-        res["graph"] = bench_graph(args, cache, inp, pos, rows, out, ws, mirror, cfg, kv_bytes)
+def bench_f16(args, hip):
+    """The decode step and the 16 x 1024 prefill with FP16 storage (same
+    kernels, FP16 operands): the same figures as the BF16 lines."""
+    K = args.f16_steps
+    d = decode_leg(args, hip, "f16", K, min(args.warmup, K), args.layers)
+    ms = d["wall"] * 1e3 / K
+    attn = float(np.mean(d["attn_ms"]))
+    kv = d["kv_bytes"]
+    res = {"decode": {"workload": f"{args.workload}_decode", "steps": K,
+                      "ms_per_step": round(ms, 4), "value": round(kv / (ms * 1e-3) / 1e9, 1),
+                      "unit": "GB/s",
+                      "roofline": {"kernel": "k_decode_stream", "bound": "hbm",
+                                   "achieved": round(kv / (attn * 1e-3) / 1e9, 1),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(kv / (attn * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                   "avg_launch_ms": round(attn, 5)}}}
+    del d
     if args.prefill_steps > 0:
-        res["prefill"] = bench_prefill(args, hip, "prefill", args.prefill_steps)
-    if args.chunk_steps > 0:
-        res["chunk"] = bench_prefill(args, hip, "chunk", args.chunk_steps)
-    if args.cpu_seconds > 0:
-        call(0)  # a fresh layer-0 step: the oracle sample is compared with it
-        torch.cuda.synchronize()
-        res["cpu_baseline"] = cpu_baseline(args, cfg, inp, layers[0], pos_h, rows_h, out)
-    print(json.dumps(res), flush=True)
+        res["prefill"] = bench_prefill(args, hip, "prefill", args.prefill_steps, dtype="f16")
+    return res
 
 
 def bench_graph(args, cache, inp, pos, rows, out, ws, mirror, cfg, kv_bytes):
@@ -315,7 +366,7 @@ def prefill_label(name):
     return f"prefill_{cfg['A']}x{cfg['T']}"
 
 
-def bench_prefill(args, hip, name, K):
+def bench_prefill(args, hip, name, K, dtype="bf16"):
     """Batched prefill, 32/8/128: "prefill" = 16 prompts x 1024 tokens into
     empty rows; "chunk" = 16 rows appending chunks of 128..512 tokens at starts
     in [0, 3072].  The attention kernel's own duration comes from events
@@ -325,7 +376,7 @@ def bench_prefill(args, hip, name, K):
     import positions_aware_cached_amd as pac
     import workloads
 
-    cfg = workloads.config(name)
+    cfg = workloads.config(name, dtype=dtype)
     A, T, Hq, Hkv, D = (cfg[k] for k in ("A", "T", "Hq", "Hkv", "D"))
     inp = workloads.draw_prefill(cfg, device="cuda")
     cache = pac.Cache.wrap([inp["Kc"]], [inp["Vc"]])
@@ -392,44 +443,52 @@ def bench_prefill(args, hip, name, K):
             "roofline": {"kernel": "k_prefill_mfma", "bound": "mfma",
                          "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                         "traffic": measured_traffic("k_prefill_mfma", label)},
+                         "traffic": measured_traffic("k_prefill_mfma", label)
+                         if dtype == "bf16" else None},
             "hbm_gbs_step": round(hbm / wall / 1e9, 1)}
 
 
-def cpu_baseline(args, cfg, inp, layer0, pos_h, rows_h, out_gpu):
+def cpu_baseline(args, cfg, inp, layers, pos_h, rows_h, out_gpu):
     """The CPU oracle (single thread, as it stands) on a bounded sample of the
     same workload: entries one by one, each on a host copy of its row's prefix,
-    until the time budget is spent.  Its outputs are also compared with the
-    GPU's layer-0 outputs for those entries."""
-    import torch
-
+    layer after layer of the rotated caches, until the time budget is spent.
+    The layer-0 outputs are also compared with the GPU's layer-0 outputs."""
     import oracle
     import workloads
 
-    Kc, Vc = layer0
     Hkv, D = cfg["Hkv"], cfg["D"]
     qb, kb, vb = (workloads.bits(inp[k]) for k in ("q", "k_new", "v_new"))
     orc = oracle.default()
+    if cfg["dtype"] == "f16":
+        widen = lambda b: np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+    else:
+        widen = oracle.bf16_to_f32
     done, kv, elapsed, worst = 0, 0, 0.0, 0.0
     t_start = time.perf_counter()
-    for a in range(len(pos_h)):
-        p, r = int(pos_h[a]), int(rows_h[a])
-        Km = workloads.bits(Kc[r, :p + 1]).reshape(1, p + 1, Hkv, D).copy()
-        Vm = workloads.bits(Vc[r, :p + 1]).reshape(1, p + 1, Hkv, D).copy()
-        t0 = time.perf_counter()
-        o = orc.decode_step(qb[a:a + 1], kb[a:a + 1], vb[a:a + 1], [p], [0], Km, Vm, cfg["base"])
-        elapsed += time.perf_counter() - t0
-        done += 1
-        kv += (p + 1) * Hkv * D * 2 * 2
-        g = workloads.bits(out_gpu[a])
-        worst = max(worst, float(np.abs(oracle.bf16_to_f32(o[0]).astype(np.float64) -
-                                        oracle.bf16_to_f32(g).astype(np.float64)).max()))
-        if elapsed >= args.cpu_seconds or time.perf_counter() - t_start > 3 * args.cpu_seconds:
-            break
-    del torch
+    out_bits = workloads.bits(out_gpu)
+    for layer, (Kc, Vc) in enumerate(layers):
+        for a in range(len(pos_h)):
+            p, r = int(pos_h[a]), int(rows_h[a])
+            Km = workloads.bits(Kc[r, :p + 1]).reshape(1, p + 1, Hkv, D).copy()
+            Vm = workloads.bits(Vc[r, :p + 1]).reshape(1, p + 1, Hkv, D).copy()
+            t0 = time.perf_counter()
+            o = orc.decode_step(qb[a:a + 1], kb[a:a + 1], vb[a:a + 1], [p], [0], Km, Vm,
+                                cfg["base"], dtype=cfg["dtype"])
+            elapsed += time.perf_counter() - t0
+            done += 1
+            kv += (p + 1) * Hkv * D * 2 * 2
+            if layer == 0:
+                worst = max(worst, float(np.abs(widen(o[0]).astype(np.float64) -
+                                                widen(out_bits[a]).astype(np.float64)).max()))
+            if elapsed >= args.cpu_seconds or time.perf_counter() - t_start > 3 * args.cpu_seconds:
+                break
+        else:
+            continue
+        break
     return {"value": round(kv / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {len(pos_h)} entries of the {args.workload} decode step "
-                      f"(layer 0), {kv} KV bytes, {elapsed:.2f} s single-threaded",
+            "sample": f"{done} entry-steps of the {args.workload} decode step ({len(pos_h)} "
+                      f"entries per layer, layers 0..{done // len(pos_h)} of the rotated "
+                      f"caches), {kv} KV bytes, {elapsed:.2f} s single-threaded",
             "tokens_per_s": round(done / elapsed, 3),
             "gpu_vs_oracle_max_abs": worst}
 
