@@ -159,6 +159,11 @@ mllm_status mllm_cache_reset_row(mllm_cache *cache, int32_t row);
  * after a decode made with a host mirror, 0 after a reset. */
 mllm_status mllm_cache_row_length(const mllm_cache *cache, int32_t row, int32_t *len);
 
+/* Declare a row's logical length, 0 <= len <= capacity (MLLM_ERR_OUT_OF_RANGE
+ * otherwise): for a caller that filled or restored the row by other means, or
+ * decoded without a host mirror.  Touches no device memory. */
+mllm_status mllm_cache_set_row_length(mllm_cache *cache, int32_t row, int32_t len);
+
 /* Workspace bytes needed by mllm_decode_rope_store_attn for A entries and h_q
  * query heads with the given opts (may be NULL).  max_position bounds every
  * position of the call (-1 = capacity - 1); this build's size does not depend
@@ -305,6 +310,75 @@ mllm_status mllm_prefill_chunk_rope_store_attn(mllm_cache *cache, int32_t layer,
                                                const mllm_tensor_view *out, void *workspace,
                                                uint64_t workspace_bytes,
                                                const mllm_decode_opts *opts, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Slot manager ("Tensor ownership boundary": a scheduler above the model
+ * primitives owns the request-to-row map, admits only at step boundaries,
+ * resets a row on length, stop or cancel and reuses the lowest free slot; the
+ * shared cache allocation persists while the rows' active prefixes fall back
+ * to zero; max_sequence_length bounds the persistent cache, zero keeping the
+ * model maximum).  Host logic over the calls above: it reads the rows'
+ * logical lengths, which the prefill and decode calls advance (the decode call
+ * with a host mirror), resets rows logically, and makes no device call.  One
+ * thread at a time per scheduler; the scheduler owns every row of its cache.
+ */
+typedef struct mllm_sched mllm_sched;
+
+/* Why a request left its row. */
+typedef enum { MLLM_END_LENGTH = 1, MLLM_END_STOP = 2, MLLM_END_CANCEL = 3 } mllm_end;
+
+/* One line of a step plan. */
+typedef struct {
+    int64_t request_id;
+    int32_t row;
+    int32_t value; /* admitted: prompt length; decode: the position the request's
+                      next token is stored at (the row's length); retired: mllm_end */
+} mllm_sched_entry;
+
+/* A scheduler over every row of `cache`; each row must be empty (length 0,
+ * else MLLM_ERR_ROW_BUSY).  max_sequence_length: 0 = the cache capacity,
+ * else 1..capacity (MLLM_ERR_OUT_OF_RANGE). */
+mllm_status mllm_sched_create(mllm_cache *cache, int32_t max_sequence_length, mllm_sched **out);
+mllm_status mllm_sched_free(mllm_sched *sched);
+/* The bound in force (the cache capacity when created with 0). */
+mllm_status mllm_sched_max_sequence_length(const mllm_sched *sched, int32_t *len);
+
+/* Queue a request, first in first out.  prompt_len >= 1, max_new_tokens >= 0
+ * (MLLM_ERR_INVALID_ARG); prompt_len + max_new_tokens <= max_sequence_length
+ * (MLLM_ERR_OUT_OF_RANGE); ids unique among queued and active requests
+ * (MLLM_ERR_INVALID_ARG). */
+mllm_status mllm_sched_submit(mllm_sched *sched, int64_t request_id, int32_t prompt_len,
+                              int32_t max_new_tokens);
+/* End a request: stop (the caller saw its stop token) takes effect at the next
+ * boundary; cancel removes a queued request at once and ends an active one at
+ * the next boundary.  Unknown id: MLLM_ERR_INVALID_ARG. */
+mllm_status mllm_sched_stop(mllm_sched *sched, int64_t request_id);
+mllm_status mllm_sched_cancel(mllm_sched *sched, int64_t request_id);
+
+/*
+ * Step boundary.  In order:
+ *  1. retire: each active request that was cancelled (MLLM_END_CANCEL) or
+ *     stopped (MLLM_END_STOP), or whose row holds prompt_len + max_new_tokens
+ *     positions (MLLM_END_LENGTH; each decode step stores one token), leaves
+ *     its row; the row is reset to length 0 and freed;
+ *  2. decode: every request admitted at an earlier boundary that remains, by
+ *     row, with the position its next token is stored at (the row's length);
+ *  3. admit: queued requests, first in first out, take the lowest free rows
+ *     while any is free; listed by prompt length, then row, so equal prompt
+ *     lengths are contiguous (one equal-length prefill group each, or one
+ *     prefill chunk call for all).  They decode from the next boundary on.
+ * The caller then runs this step: the prefill of the admitted rows and the
+ * decode of the decode list (with a host mirror, so the row lengths advance).
+ * Each array is caller-owned with room for at least `slots` entries
+ * (MLLM_ERR_INVALID_ARG otherwise, nothing changed).
+ */
+mllm_status mllm_sched_boundary(mllm_sched *sched, mllm_sched_entry *admitted,
+                                int32_t admitted_cap, int32_t *n_admitted,
+                                mllm_sched_entry *decode, int32_t decode_cap, int32_t *n_decode,
+                                mllm_sched_entry *retired, int32_t retired_cap,
+                                int32_t *n_retired);
+/* Requests waiting in the queue and requests holding a row. */
+mllm_status mllm_sched_counts(const mllm_sched *sched, int32_t *queued, int32_t *active);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,10 @@ EXPORTS = ("mllm_abi_version", "mllm_last_error", "mllm_cache_bytes", "mllm_cach
            "mllm_cache_wrap", "mllm_cache_free", "mllm_cache_layer", "mllm_cache_get_desc",
            "mllm_cache_reset_row", "mllm_cache_row_length", "mllm_decode_workspace_size",
            "mllm_decode_rope_store_attn", "mllm_prefill_workspace_size",
-           "mllm_prefill_rope_store_attn", "mllm_prefill_chunk_rope_store_attn")
+           "mllm_prefill_rope_store_attn", "mllm_prefill_chunk_rope_store_attn",
+           "mllm_cache_set_row_length", "mllm_sched_create", "mllm_sched_free",
+           "mllm_sched_max_sequence_length", "mllm_sched_submit", "mllm_sched_stop",
+           "mllm_sched_cancel", "mllm_sched_boundary", "mllm_sched_counts")
 
 
 class MllmError(RuntimeError):
@@ -56,6 +59,13 @@ class RopeDesc(ctypes.Structure):
 
 
 MAX_WAVES = 4096  # largest wave count a decode launch accepts
+
+
+class SchedEntry(ctypes.Structure):
+    _fields_ = [("request_id", ctypes.c_int64), ("row", ctypes.c_int32), ("value", ctypes.c_int32)]
+
+
+END_REASONS = {1: "length", 2: "stop", 3: "cancel"}
 
 
 class DecodeOpts(ctypes.Structure):
@@ -89,6 +99,16 @@ def load(path=LIB_PATH):
     L.mllm_cache_get_desc.argtypes = [vp, P(CacheDesc)]
     L.mllm_cache_reset_row.argtypes = [vp, i32]
     L.mllm_cache_row_length.argtypes = [vp, i32, P(i32)]
+    L.mllm_cache_set_row_length.argtypes = [vp, i32, i32]
+    L.mllm_sched_create.argtypes = [vp, i32, P(vp)]
+    L.mllm_sched_free.argtypes = [vp]
+    L.mllm_sched_max_sequence_length.argtypes = [vp, P(i32)]
+    L.mllm_sched_submit.argtypes = [vp, ctypes.c_int64, i32, i32]
+    L.mllm_sched_stop.argtypes = [vp, ctypes.c_int64]
+    L.mllm_sched_cancel.argtypes = [vp, ctypes.c_int64]
+    L.mllm_sched_boundary.argtypes = [vp, P(SchedEntry), i32, P(i32), P(SchedEntry), i32, P(i32),
+                                      P(SchedEntry), i32, P(i32)]
+    L.mllm_sched_counts.argtypes = [vp, P(i32), P(i32)]
     L.mllm_decode_workspace_size.argtypes = [vp, i32, i32, i32, P(DecodeOpts), P(u64)]
     L.mllm_decode_rope_store_attn.argtypes = [
         vp, i32, P(TensorView), P(TensorView), P(TensorView), vp, vp, i32, P(i32),
@@ -219,6 +239,59 @@ class Cache:
         n = ctypes.c_int32()
         _check(load().mllm_cache_row_length(self.handle, row, ctypes.byref(n)))
         return n.value
+
+    def set_row_length(self, row, length):
+        _check(load().mllm_cache_set_row_length(self.handle, row, length))
+
+
+class Scheduler:
+    """The slot manager over a cache (see mllm_sched_* in include/mllm.h)."""
+
+    def __init__(self, cache, max_sequence_length=0):
+        self.cache = cache  # kept alive: the scheduler reads and resets its rows
+        self.slots = cache.desc.slots
+        h = ctypes.c_void_p()
+        _check(load().mllm_sched_create(cache.handle, max_sequence_length, ctypes.byref(h)))
+        self.handle = h
+        n = ctypes.c_int32()
+        _check(load().mllm_sched_max_sequence_length(self.handle, ctypes.byref(n)))
+        self.max_sequence_length = n.value
+
+    def submit(self, request_id, prompt_len, max_new_tokens):
+        _check(load().mllm_sched_submit(self.handle, request_id, prompt_len, max_new_tokens))
+
+    def stop(self, request_id):
+        _check(load().mllm_sched_stop(self.handle, request_id))
+
+    def cancel(self, request_id):
+        _check(load().mllm_sched_cancel(self.handle, request_id))
+
+    def boundary(self):
+        """One step boundary -> (admitted, decode, retired), each a list of
+        (request_id, row, value) tuples (value: prompt length, position, end reason)."""
+        arrs = [(SchedEntry * self.slots)() for _ in range(3)]
+        ns = [ctypes.c_int32() for _ in range(3)]
+        _check(load().mllm_sched_boundary(
+            self.handle, arrs[0], self.slots, ctypes.byref(ns[0]), arrs[1], self.slots,
+            ctypes.byref(ns[1]), arrs[2], self.slots, ctypes.byref(ns[2])))
+        return tuple([(e.request_id, e.row, e.value) for e in a[:n.value]]
+                     for a, n in zip(arrs, ns))
+
+    def counts(self):
+        q, a = ctypes.c_int32(), ctypes.c_int32()
+        _check(load().mllm_sched_counts(self.handle, ctypes.byref(q), ctypes.byref(a)))
+        return q.value, a.value
+
+    def free(self):
+        if self.handle:
+            _check(load().mllm_sched_free(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
 
 
 def decode_workspace_size(cache, A, h_q, max_position=-1, waves=0, kernel=0):

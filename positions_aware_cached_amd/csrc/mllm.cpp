@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "../../include/mllm.h"
+#include "host.h"
 #include "kernels.h"
 
 struct mllm_cache {
@@ -50,6 +51,21 @@ mllm_status ok()
     g_error.clear();
     return MLLM_OK;
 }
+
+}  // namespace
+
+namespace mllm {
+
+mllm_status host_fail(mllm_status st, const char *msg)
+{
+    return fail(st, "%s", msg);
+}
+
+mllm_status host_ok() { return ok(); }
+
+}  // namespace mllm
+
+namespace {
 
 mllm_status hip_fail(hipError_t e, const char *what)
 {
@@ -365,6 +381,20 @@ mllm_status mllm_cache_reset_row(mllm_cache *cache, int32_t row)
         return fail(MLLM_ERR_OUT_OF_RANGE, "row %d out of range [0, %d)", row,
                     cache->desc.slots);
     cache->length[row] = 0;
+    return ok();
+}
+
+mllm_status mllm_cache_set_row_length(mllm_cache *cache, int32_t row, int32_t len)
+{
+    if (!cache)
+        return fail(MLLM_ERR_INVALID_ARG, "cache is null");
+    if (row < 0 || row >= cache->desc.slots)
+        return fail(MLLM_ERR_OUT_OF_RANGE, "row %d out of range [0, %d)", row,
+                    cache->desc.slots);
+    if (len < 0 || len > cache->desc.capacity)
+        return fail(MLLM_ERR_OUT_OF_RANGE, "length %d outside [0, capacity %d]", len,
+                    cache->desc.capacity);
+    cache->length[row] = len;
     return ok();
 }
 
