@@ -52,6 +52,8 @@ def parse():
                     help="also time the prefill chunk of mixed starts and lengths (0 = skip)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
                     help="storage type of the cache and tensors of the headline run")
+    ap.add_argument("--sched-boundaries", type=int, default=2000,
+                    help="also time the slot manager's step boundary (0 = skip)")
     ap.add_argument("--f16-steps", type=int, default=50,
                     help="also time the decode step and the prefill with FP16 storage (0 = skip)")
     ap.add_argument("--copy-reference", action="store_true",
@@ -208,6 +210,8 @@ def main():
         res["chunk"] = bench_prefill(args, hip, "chunk", args.chunk_steps)
     if args.f16_steps > 0 and args.dtype != "f16":
         res["f16"] = bench_f16(args, hip)
+    if args.sched_boundaries > 0:
+        res["sched"] = bench_sched(args, ms_per_step)
     if args.cpu_seconds > 0:
         call(0)  # a fresh layer-0 step: the oracle sample is compared with it
         torch.cuda.synchronize()
@@ -318,6 +322,43 @@ def bench_f16(args, hip):
     if args.prefill_steps > 0:
         res["prefill"] = bench_prefill(args, hip, "prefill", args.prefill_steps, dtype="f16")
     return res
+
+
+def bench_sched(args, step_ms):
+    """Host cost of the slot manager's step boundary in steady serving: 64 rows
+    (the decode batch of the headline workload), requests of 128-512 prompt and
+    64-256 new tokens arriving so that the queue never empties; row lengths are
+    advanced as the prefill and decode calls would.  Timed: the boundary calls
+    only, through the Python binding (ctypes included)."""
+    import random
+
+    import torch
+
+    import positions_aware_cached_amd as pac
+
+    S, C = 64, 1024
+    K = torch.empty((S, C, 1, 64), dtype=torch.bfloat16, device="cuda")
+    cache = pac.Cache.wrap([K], [torch.empty_like(K)])
+    sched = pac.Scheduler(cache)
+    rng = random.Random(0)
+    next_id, spent, n_adm, n_ret = 0, 0.0, 0, 0
+    for i in range(args.sched_boundaries):
+        while sched.counts()[0] < 8:
+            sched.submit(next_id, rng.randint(128, 512), rng.randint(64, 256))
+            next_id += 1
+        t0 = time.perf_counter()
+        admitted, decode, retired = sched.boundary()
+        spent += time.perf_counter() - t0
+        n_adm += len(admitted)
+        n_ret += len(retired)
+        for _, row, prompt in admitted:
+            cache.set_row_length(row, prompt)
+        for _, row, pos in decode:
+            cache.set_row_length(row, pos + 1)
+    us = spent / args.sched_boundaries * 1e6
+    return {"slots": S, "boundaries": args.sched_boundaries, "boundary_us": round(us, 2),
+            "admitted": n_adm, "retired": n_ret,
+            "fraction_of_decode_step": round(us * 1e-3 / step_ms, 4)}
 
 
 def bench_graph(args, cache, inp, pos, rows, out, ws, mirror, cfg, kv_bytes):
