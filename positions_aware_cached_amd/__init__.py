@@ -256,6 +256,12 @@ class Scheduler:
         n = ctypes.c_int32()
         _check(load().mllm_sched_max_sequence_length(self.handle, ctypes.byref(n)))
         self.max_sequence_length = n.value
+        # plan arrays and counts, reused by every boundary call
+        self._arrs = [(SchedEntry * self.slots)() for _ in range(3)]
+        self._ns = [ctypes.c_int32() for _ in range(3)]
+        self._args = (self.handle, self._arrs[0], self.slots, ctypes.byref(self._ns[0]),
+                      self._arrs[1], self.slots, ctypes.byref(self._ns[1]), self._arrs[2],
+                      self.slots, ctypes.byref(self._ns[2]))
 
     def submit(self, request_id, prompt_len, max_new_tokens):
         _check(load().mllm_sched_submit(self.handle, request_id, prompt_len, max_new_tokens))
@@ -269,13 +275,9 @@ class Scheduler:
     def boundary(self):
         """One step boundary -> (admitted, decode, retired), each a list of
         (request_id, row, value) tuples (value: prompt length, position, end reason)."""
-        arrs = [(SchedEntry * self.slots)() for _ in range(3)]
-        ns = [ctypes.c_int32() for _ in range(3)]
-        _check(load().mllm_sched_boundary(
-            self.handle, arrs[0], self.slots, ctypes.byref(ns[0]), arrs[1], self.slots,
-            ctypes.byref(ns[1]), arrs[2], self.slots, ctypes.byref(ns[2])))
+        _check(load().mllm_sched_boundary(*self._args))
         return tuple([(e.request_id, e.row, e.value) for e in a[:n.value]]
-                     for a, n in zip(arrs, ns))
+                     for a, n in zip(self._arrs, self._ns))
 
     def counts(self):
         q, a = ctypes.c_int32(), ctypes.c_int32()
