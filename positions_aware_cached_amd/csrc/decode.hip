@@ -770,18 +770,23 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
 
 // ---------------------------------------------------------------- R4
 // One wave per (entry, query head): the partials of segment (a, h = hq / G)
-// sit in slots seg + w for the waves w that touched it (the same plan as the
-// decode kernel); they are summed with weights 2^(m_w - M) (loads issued four
-// at a time), divided by the weighted sum of l_w and rounded to the storage
-// type.  An
-// entry with an out-of-range position or row gets a NaN output and sets the
-// status word.
+// sit in slots seg + w for the groups w that touched it (the same plan as the
+// decode kernel); they are summed with weights 2^(m_w - M), divided by the
+// weighted sum of l_w and rounded to the storage type.  An entry with an
+// out-of-range position or row gets a NaN output and sets the status word.
+// The loads are issued in as few round trips as the data allows: the entry's
+// own indices together with the plan's, then every (max, sum) pair together
+// with up to kMergeBatch partial outputs per lane.
+constexpr int kMergeBatch = 16;
+
 template <class E, int D>
 __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
 {
     constexpr int PER = D / 64;
     const int hq = blockIdx.x, a = blockIdx.y, lane = threadIdx.x;
     const int pos = p.positions[a], row = p.rows[a];
+    long long NT, before;
+    plan_sums(p, a, lane, NT, before);
     uint16_t *out = p.out + a * p.o_sa + hq * p.o_sh;
     if (!entry_valid(p, pos, row)) {
 #pragma unroll
@@ -793,52 +798,65 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
     }
     const int G = p.G, h = hq / G, g = hq - h * G, HG = p.HG, NHG = p.NHG;
     const int hg = h / HG, wi = h - hg * HG;  // head group, wave of the group
-    long long NT, before;
-    plan_sums(p, a, lane, NT, before);  // NT >= 1: this entry is valid
-    const int NW = plan_waves(p.NS, NT);
+    const int NW = plan_waves(p.NS, NT);      // NT >= 1: this entry is valid
     const int na = (pos + kTile) / kTile;
     const long long ts = before + (long long)hg * na;
     const int wf = plan_wave_of(ts, NT, NW), wl = plan_wave_of(ts + na - 1, NT, NW);
     const int ns = wl - wf + 1;
-    // slot of the partial of group wf + x for this head
-    auto slot_of = [&](int x) { return (size_t)(a * NHG + hg + wf + x) * HG + wi; };
-    float M = -INFINITY;
-    for (int c = lane; c < ns; c += 64)
-        M = fmaxf(M, p.part_ml[(slot_of(c) * G + g) * 2]);
-    M = wave_max(M);
+    // partial of group wf + x for this head: (max, sum) and D outputs
+    auto slot_of = [&](int x) { return ((size_t)(a * NHG + hg + wf + x) * HG + wi) * G + g; };
     float lw = 0.0f, O[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e)
         O[e] = 0.0f;
+    float M = -INFINITY;
     for (int c = 0; c < ns; c += 64) {
-        float wgt = 0.0f;
+        // lane u holds the (max, sum) of slot c + u; every lane loads its
+        // elements of the first batch of outputs in the same round trip
+        float m_u = -INFINITY, l_u = 0.0f;
         if (c + lane < ns) {
-            const float *ml = p.part_ml + (slot_of(c + lane) * G + g) * 2;
-            wgt = exp2f(ml[0] - M);
-            lw += wgt * ml[1];
+            const float2 ml = *(const float2 *)(p.part_ml + slot_of(c + lane) * 2);
+            m_u = ml.x;
+            l_u = ml.y;
         }
         const int cnt = min(64, ns - c);
-        int k = 0;
-        for (; k + 4 <= cnt; k += 4) {
-            float wk[4], x[4][PER];
+        float x[kMergeBatch][PER];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                wk[u] = __shfl(wgt, k + u, 64);
-#pragma unroll
-                for (int e = 0; e < PER; ++e)
-                    x[u][e] = p.part_o[(slot_of(c + k + u) * G + g) * D + lane + 64 * e];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int e = 0; e < PER; ++e)
-                    O[e] += wk[u] * x[u][e];
-        }
-        for (; k < cnt; ++k) {
-            const float wk = __shfl(wgt, k, 64);
+        for (int u = 0; u < kMergeBatch; ++u)
 #pragma unroll
             for (int e = 0; e < PER; ++e)
-                O[e] += wk * p.part_o[(slot_of(c + k) * G + g) * D + lane + 64 * e];
+                x[u][e] = u < cnt ? p.part_o[slot_of(c + u) * D + lane + 64 * e] : 0.0f;
+        // rescale what earlier batches of 64 slots summed to the new maximum
+        const float m_new = fmaxf(M, wave_max(m_u));
+        const float alpha = exp2f(M - m_new);  // 0 on the first batch (M = -inf)
+        lw *= alpha;
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            O[e] *= alpha;
+        M = m_new;
+        const float wgt = c + lane < ns ? exp2f(m_u - M) : 0.0f;
+        lw += wgt * l_u;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const float wk = __shfl(wgt, u, 64);
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                O[e] += wk * x[u][e];
+        }
+        for (int k = kMergeBatch; k < cnt; k += kMergeBatch) {
+            const int left = min(kMergeBatch, cnt - k);
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u)
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    x[u][e] = u < left ? p.part_o[slot_of(c + k + u) * D + lane + 64 * e] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const float wk = __shfl(wgt, k + u, 64);
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    O[e] += wk * x[u][e];
+            }
         }
     }
     const float L = wave_sum(lw);
