@@ -208,8 +208,9 @@ mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32
  *  status_dev      : NULL or device int32, set to 1 on a device-side index
  *                    error, never cleared by the library.
  *  stream          : hipStream_t (NULL = the null stream).
- *  A = 0 is a successful no-op.  The call is idempotent (same inputs give the
- *  same cache bytes and output bits).
+ *  A = 0 is a successful no-op; A * h_q must stay below 2^31
+ *  (MLLM_ERR_UNSUPPORTED).  The call is idempotent (same inputs give the same
+ *  cache bytes and output bits).
  */
 mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
                                         const mllm_tensor_view *q,
@@ -245,7 +246,8 @@ mllm_status mllm_prefill_workspace_size(const mllm_cache *cache, int32_t A, int3
  *  cache_rows_dev  : device int32[A]; cache_rows_host: host int32[A], the
  *                    same values (required: rows are checked in range,
  *                    distinct and logically empty, else MLLM_ERR_ROW_BUSY).
- *  1 <= T <= capacity.  On success every target row's length becomes T.
+ *  1 <= T <= capacity; A * T * H_q must stay below 2^31 (MLLM_ERR_UNSUPPORTED).
+ *  On success every target row's length becomes T.
  *  opts (may be NULL): kernel 0 = matrix-core kernel, 1 = readable kernel;
  *  attn_events timestamps the attention kernel; waves is ignored.
  *  Other arguments as for the decode call.

@@ -122,7 +122,9 @@ template <class E, int D>
 __global__ __launch_bounds__(64) void k_decode_readable(DecodeParams p)
 {
     constexpr int PER = D / 64;
-    const int hq = blockIdx.x, a = blockIdx.y, lane = threadIdx.x;
+    // one-dimensional grid of A * Hq waves (the y and z grid sizes are limited)
+    const int hq = (int)(blockIdx.x % (unsigned)p.Hq), a = (int)(blockIdx.x / (unsigned)p.Hq);
+    const int lane = threadIdx.x;
     const int pos = p.positions[a], row = p.rows[a];
     uint16_t *out = p.out + a * p.o_sa + hq * p.o_sh;
     if (!entry_valid(p, pos, row)) {
@@ -385,6 +387,24 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     long long NT, unused;
     plan_sums(p, 0, lane, NT, unused);
     const int NW = plan_waves(p.NS, NT);
+    if (w == 0 && wi == 0) {
+        // the plan's prefix for the merge kernel: tiles before each entry, then NT
+        long long run = 0;
+        for (int c0 = 0; c0 < p.A; c0 += 256) {
+            EntryBlock b;
+            load_block(p, c0, lane, b);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int incl = wave_incl_scan(b.na[k], lane);
+                const int x = c0 + 64 * k + lane;
+                if (x < p.A)
+                    p.plan[x] = run + (long long)NHG * (incl - b.na[k]);
+                run += (long long)NHG * __shfl(incl, 63, 64);
+            }
+        }
+        if (lane == 0)
+            p.plan[p.A] = run;
+    }
     if (w >= NW)
         return;
     const long long t0 = (long long)w * NT / NW, t1 = (long long)(w + 1) * NT / NW;
@@ -770,23 +790,25 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
 
 // ---------------------------------------------------------------- R4
 // One wave per (entry, query head): the partials of segment (a, h = hq / G)
-// sit in slots seg + w for the groups w that touched it (the same plan as the
-// decode kernel); they are summed with weights 2^(m_w - M), divided by the
-// weighted sum of l_w and rounded to the storage type.  An entry with an
-// out-of-range position or row gets a NaN output and sets the status word.
-// The loads are issued in as few round trips as the data allows: the entry's
-// own indices together with the plan's, then every (max, sum) pair together
-// with up to kMergeBatch partial outputs per lane.
+// sit in slots seg + w for the groups w that touched it (the plan of the
+// decode kernel, whose prefix it left in the workspace); they are summed with
+// weights 2^(m_w - M), divided by the weighted sum of l_w and rounded to the
+// storage type.  An entry with an out-of-range position or row gets a NaN
+// output and sets the status word.  The loads are issued in as few round trips
+// as the data allows: the entry's indices together with its plan prefix, then
+// every (max, sum) pair together with up to kMergeBatch partial outputs per
+// lane.
 constexpr int kMergeBatch = 16;
 
 template <class E, int D>
 __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
 {
     constexpr int PER = D / 64;
-    const int hq = blockIdx.x, a = blockIdx.y, lane = threadIdx.x;
+    // one-dimensional grid of A * Hq waves (the y and z grid sizes are limited)
+    const int hq = (int)(blockIdx.x % (unsigned)p.Hq), a = (int)(blockIdx.x / (unsigned)p.Hq);
+    const int lane = threadIdx.x;
     const int pos = p.positions[a], row = p.rows[a];
-    long long NT, before;
-    plan_sums(p, a, lane, NT, before);
+    const long long before = p.plan[a], NT = p.plan[p.A];
     uint16_t *out = p.out + a * p.o_sa + hq * p.o_sh;
     if (!entry_valid(p, pos, row)) {
 #pragma unroll
@@ -877,7 +899,8 @@ DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t Hkv, int6
     const uint64_t slots = ((uint64_t)A * Hkv + NS) * (Hq / Hkv);
     w.part_o_off = up(w.qrot_off + (uint64_t)A * Hq * D * 4);
     w.part_ml_off = up(w.part_o_off + slots * D * 4);
-    w.total = up(w.part_ml_off + slots * 2 * 4);
+    w.plan_off = up(w.part_ml_off + slots * 2 * 4);
+    w.total = up(w.plan_off + ((uint64_t)A + 1) * 8);
     return w;
 }
 
@@ -942,7 +965,7 @@ hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEve
 template <class E>
 static void launch_merge_e(const DecodeParams &p, hipStream_t stream)
 {
-    const dim3 grid(p.Hq, p.A), block(64);
+    const dim3 grid(p.Hq * p.A), block(64);
     if (p.D == 64)
         hipLaunchKernelGGL((k_decode_merge<E, 64>), grid, block, 0, stream, p);
     else
@@ -1006,7 +1029,7 @@ int decode_resident_groups(int device, int D, int G, int HG, int dtype)
 template <class E>
 static void launch_readable_e(const DecodeParams &p, hipStream_t stream, hipEvent_t e0, hipEvent_t e1)
 {
-    const dim3 grid(p.Hq, p.A), block(64);
+    const dim3 grid(p.Hq * p.A), block(64);
     if (p.D == 64)
         hipExtLaunchKernelGGL((k_decode_readable<E, 64>), grid, block, 0, stream, e0, e1, 0, p);
     else

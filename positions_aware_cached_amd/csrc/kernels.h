@@ -24,6 +24,7 @@ struct DecodeParams {
     float *qrot;      // workspace [A, Hq, D]      rotated queries, FP32
     float *part_o;    // workspace [slots, G, D]  per (segment, group, head) unnormalized outputs
     float *part_ml;   // workspace [slots, G, 2]  per (segment, group, head) (max, sum), log2 domain
+    long long *plan;  // workspace [A + 1]: tiles before each entry (x NHG), then the total NT
     int32_t *status;  // optional device status word
     int32_t dtype;     // storage type of every 16-bit tensor: 1 BF16, 2 FP16
     int32_t A, S, C, Hq, Hkv, D, G;
@@ -35,7 +36,7 @@ struct DecodeParams {
 
 // Workspace carve-up for a decode step (all offsets 256-byte aligned).
 struct DecodeWorkspace {
-    uint64_t qrot_off, part_o_off, part_ml_off, total;
+    uint64_t qrot_off, part_o_off, part_ml_off, plan_off, total;
 };
 DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t Hkv, int64_t D,
                                         int64_t NS);

@@ -464,6 +464,9 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
         return fail(MLLM_ERR_INVALID_ARG, "H_q %lld must be a positive multiple of H_kv %d",
                     (long long)Hq, d.h_kv);
     const int G = (int)(Hq / d.h_kv);
+    if ((int64_t)A * Hq >= (1ll << 31))
+        return fail(MLLM_ERR_UNSUPPORTED, "A * H_q = %lld must stay below 2^31 (one wave each)",
+                    (long long)A * Hq);
     if (G > 16)
         return fail(MLLM_ERR_UNSUPPORTED, "group size H_q/H_kv = %d exceeds 16", G);
     mllm_status st = check_rope(rope, D);
@@ -550,6 +553,7 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     p.qrot = (float *)((char *)workspace + wl.qrot_off);
     p.part_o = (float *)((char *)workspace + wl.part_o_off);
     p.part_ml = (float *)((char *)workspace + wl.part_ml_off);
+    p.plan = (long long *)((char *)workspace + wl.plan_off);
     p.status = status_dev;
     p.A = A;
     p.S = d.slots;
@@ -642,6 +646,9 @@ mllm_status prefill_call(mllm_cache *cache, int32_t layer, const mllm_tensor_vie
         return fail(MLLM_ERR_INVALID_ARG, "H_q %lld must be a positive multiple of H_kv %d",
                     (long long)Hq, d.h_kv);
     const int G = (int)(Hq / d.h_kv);
+    if ((int64_t)A * T * Hq >= (1ll << 31))
+        return fail(MLLM_ERR_UNSUPPORTED, "A * T * H_q = %lld must stay below 2^31",
+                    (long long)A * T * Hq);
     mllm_status st = check_rope(rope, D);
     if (st)
         return st;

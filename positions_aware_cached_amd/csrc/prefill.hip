@@ -74,7 +74,9 @@ __device__ __forceinline__ Chunk chunk_of(const PrefillParams &p, int a)
 template <class E>
 __global__ __launch_bounds__(256) void k_prefill_store(PrefillParams p, float2 *table)
 {
-    const int t = blockIdx.x, a = blockIdx.y, tid = threadIdx.x;
+    // one-dimensional grid of A * T blocks (the y and z grid sizes are limited)
+    const int t = (int)(blockIdx.x % (unsigned)p.T), a = (int)(blockIdx.x / (unsigned)p.T);
+    const int tid = threadIdx.x;
     const int D = p.D, H = D / 2;
     const Chunk ch = chunk_of(p, a);
     if (!ch.ok || t >= ch.n)
@@ -121,7 +123,10 @@ template <class E, int D>
 __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const float2 *table)
 {
     constexpr int H = D / 2;
-    const int hq = blockIdx.x, t = blockIdx.y, a = blockIdx.z, lane = threadIdx.x;
+    // one-dimensional grid of A * T * Hq waves
+    const unsigned at = blockIdx.x / (unsigned)p.Hq;
+    const int hq = (int)(blockIdx.x % (unsigned)p.Hq), t = (int)(at % (unsigned)p.T),
+              a = (int)(at / (unsigned)p.T), lane = threadIdx.x;
     const Chunk ch = chunk_of(p, a);
     uint16_t *out = p.out + a * p.o_sa + t * p.o_st + hq * p.o_sh;
     if (!ch.ok) {  // device values disagree with the checked host copy: NaN output
@@ -500,7 +505,7 @@ static void launch_prefill_e(const PrefillParams &p, hipStream_t stream, int ker
 {
     const float2 *table = p.table;
     if (kernel == 1) {
-        const dim3 grid(p.Hq, p.T, p.A);
+        const dim3 grid(p.Hq * p.T * p.A);
         if (p.D == 64)
             hipExtLaunchKernelGGL((k_prefill_readable<E, 64>), grid, dim3(64), 0, stream, e0, e1, 0,
                                   p, table);
@@ -522,9 +527,9 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream, int kernel
                           hipEvent_t e1)
 {
     if (p.dtype == F16::code)
-        hipLaunchKernelGGL(k_prefill_store<F16>, dim3(p.T, p.A), dim3(256), 0, stream, p, p.table);
+        hipLaunchKernelGGL(k_prefill_store<F16>, dim3(p.T * p.A), dim3(256), 0, stream, p, p.table);
     else
-        hipLaunchKernelGGL(k_prefill_store<Bf16>, dim3(p.T, p.A), dim3(256), 0, stream, p, p.table);
+        hipLaunchKernelGGL(k_prefill_store<Bf16>, dim3(p.T * p.A), dim3(256), 0, stream, p, p.table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

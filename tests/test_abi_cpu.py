@@ -311,3 +311,12 @@ def test_dtype_rules():
     expect(pac.load().mllm_cache_wrap(ctypes.byref(d), ks, vs, ctypes.byref(h)), "UNSUPPORTED")
     assert pac.cache_bytes(1, 2, 16, 1, 64, dtype=pac.torch.float16) == \
         pac.cache_bytes(1, 2, 16, 1, 64)
+
+
+def test_grid_size_limits():
+    """Flattened launch grids: A * H_q (decode) and A * T * H_q (prefill) must
+    stay below 2^31."""
+    fc = FakeCache(S=8, C=256)
+    big = 1 << 29
+    expect(call_decode(fc, A=big, Hq=4, mirror=None), "UNSUPPORTED")
+    expect(call_prefill(fc, A=2, T=256, Hq=big // 64 * 32, rows_host=(0, 1)), "UNSUPPORTED")
