@@ -10,7 +10,7 @@
 // tokens only (prompts of different lengths in one batch); s = 0, n = T is the
 // page's equal-length prefill into empty rows.
 //
-//   k_prefill_store     one block per (token t, entry a): split-half RoPE of
+//   k_prefill_store     one wave per (token t, entry a): split-half RoPE of
 //                       k_new -> store in the storage type, v_new bit copy; the block also
 //                       writes the FP32 cos/sin table row of (a, t).
 //   k_prefill_mfma      the tuned attention: one workgroup of four waves per
@@ -70,39 +70,51 @@ __device__ __forceinline__ Chunk chunk_of(const PrefillParams &p, int a)
 }
 
 // workspace: cos/sin table [A][T][D/2] of float2 (cos, sin), row (a, t) for
-// position s_a + t
+// position s_a + t.  One wave per token: cos/sin of its D/2 angles once (into
+// LDS and the table), then each lane rotates 8 pairs of a kv head with 16-byte
+// loads and stores, and V moves in 16-byte chunks.
 template <class E>
-__global__ __launch_bounds__(256) void k_prefill_store(PrefillParams p, float2 *table)
+__global__ __launch_bounds__(64) void k_prefill_store(PrefillParams p, float2 *table)
 {
-    // one-dimensional grid of A * T blocks (the y and z grid sizes are limited)
+    // one-dimensional grid of A * T waves (the y and z grid sizes are limited)
     const int t = (int)(blockIdx.x % (unsigned)p.T), a = (int)(blockIdx.x / (unsigned)p.T);
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x;
     const int D = p.D, H = D / 2;
     const Chunk ch = chunk_of(p, a);
     if (!ch.ok || t >= ch.n)
         return;  // past the entry's length, or an invalid entry: write nothing
     const int pos = ch.s + t;
     __shared__ float cs[kMaxHalfDim], sn[kMaxHalfDim];
-    if (tid < H) {
-        float theta = __fmul_rn((float)pos, p.inv_freq[tid]);
-        cs[tid] = (float)cos((double)theta);
-        sn[tid] = (float)sin((double)theta);
-        table[((size_t)a * p.T + t) * H + tid] = make_float2(cs[tid], sn[tid]);
+    if (lane < H) {
+        float theta = __fmul_rn((float)pos, p.inv_freq[lane]);
+        cs[lane] = (float)cos((double)theta);
+        sn[lane] = (float)sin((double)theta);
+        table[((size_t)a * p.T + t) * H + lane] = make_float2(cs[lane], sn[lane]);
     }
     __syncthreads();
     const size_t slot = (size_t)p.Hkv * D;
     const size_t dst = ((size_t)ch.row * p.C + pos) * slot;
-    for (int idx = tid; idx < p.Hkv * H; idx += blockDim.x) {
-        const int h = idx / H, i = idx - h * H;
-        const uint16_t *k = p.k_new + a * p.kn_sa + t * p.kn_st + h * p.kn_sh;
-        float lo, hi;
-        rope_pair(E::to_f(k[i]), E::to_f(k[i + H]), cs[i], sn[i], lo, hi);
-        uint16_t *kd = p.kc + dst + (size_t)h * D;
-        kd[i] = (uint16_t)E::from_f(lo);
-        kd[i + H] = (uint16_t)E::from_f(hi);
+    const int CH = H / 8;  // 16-byte chunks per half head
+    for (int idx = lane; idx < p.Hkv * CH; idx += 64) {
+        const int h = idx / CH, c = idx - h * CH;
+        const uint16_t *k = p.k_new + a * p.kn_sa + t * p.kn_st + h * p.kn_sh + c * 8;
+        const u32x4 x4 = *(const u32x4 *)k, y4 = *(const u32x4 *)(k + H);
+        u32x4 lo4, hi4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i0 = c * 8 + 2 * e, i1 = i0 + 1;
+            float l0, h0, l1, h1;
+            rope_pair(E::lo(x4[e]), E::lo(y4[e]), cs[i0], sn[i0], l0, h0);
+            rope_pair(E::hi(x4[e]), E::hi(y4[e]), cs[i1], sn[i1], l1, h1);
+            lo4[e] = E::from_f(l0) | (E::from_f(l1) << 16);
+            hi4[e] = E::from_f(h0) | (E::from_f(h1) << 16);
+        }
+        uint16_t *kd = p.kc + dst + (size_t)h * D + c * 8;
+        *(u32x4 *)kd = lo4;
+        *(u32x4 *)(kd + H) = hi4;
     }
     const int chunks = D / 8;
-    for (int idx = tid; idx < p.Hkv * chunks; idx += blockDim.x) {
+    for (int idx = lane; idx < p.Hkv * chunks; idx += 64) {
         const int h = idx / chunks, c = idx - h * chunks;
         const u32x4 v = *(const u32x4 *)(p.v_new + a * p.vn_sa + t * p.vn_st + h * p.vn_sh + c * 8);
         *(u32x4 *)(p.vc + dst + (size_t)h * D + c * 8) = v;
@@ -527,9 +539,9 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream, int kernel
                           hipEvent_t e1)
 {
     if (p.dtype == F16::code)
-        hipLaunchKernelGGL(k_prefill_store<F16>, dim3(p.T * p.A), dim3(256), 0, stream, p, p.table);
+        hipLaunchKernelGGL(k_prefill_store<F16>, dim3(p.T * p.A), dim3(64), 0, stream, p, p.table);
     else
-        hipLaunchKernelGGL(k_prefill_store<Bf16>, dim3(p.T * p.A), dim3(256), 0, stream, p, p.table);
+        hipLaunchKernelGGL(k_prefill_store<Bf16>, dim3(p.T * p.A), dim3(64), 0, stream, p, p.table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
