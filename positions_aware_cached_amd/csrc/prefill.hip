@@ -41,6 +41,14 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds_base)
                                      (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
+// Lanes l and l ^ 32 exchange a value: v_permlane32_swap on two copies
+// leaves the low half's values in one register and the high half's in the
+// other, in every lane.
+__device__ __forceinline__ void swap_halves(float &a, float &b)
+{
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
 // Split-half rotation of one pair, every product and sum rounded separately
 // (contraction into fused multiply-adds is switched off: the rounding of the
 // result to the storage type must see the same FP32 value as a separately
@@ -243,18 +251,25 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
 
     const int nqt = (p.T + BM - 1) / BM;
     // Work groups are handed to the eight XCDs in turn (group b to XCD b % 8),
-    // and each XCD has its own L2.  The G query heads of a kv head read the same
-    // K/V tiles, so all blocks of one (entry, kv head) pair go to one XCD: pair
-    // i lives on XCD i % 8.  Each XCD runs its blocks longest query tile first
-    // (the tile rank is the slowest index), its pairs and heads within a rank.
+    // and each XCD has its own L2.  The G query heads and all query tiles of a kv
+    // head read the same K/V tiles, so all blocks of one (entry, kv head) pair go
+    // to one XCD: pair i lives on XCD i % 8.  An XCD takes its pairs in chunks of
+    // PG, so that the K/V rows in use at once fit its L2 (all of an XCD's pairs
+    // at once did not: every tile was fetched several times), and runs a chunk's
+    // blocks longest query tile first (the tile rank is the slowest index within
+    // the chunk), its pairs and heads within a rank.
     int qt, hq, a;
     {
         const int b = blockIdx.x, npairs = p.A * p.Hkv;
         if ((npairs & 7) == 0) {
+            constexpr int PG = 4;
+            const int ppx = npairs >> 3;  // pairs per XCD
             const int x = b & 7, j = b >> 3;
-            const int per = (npairs >> 3) * p.G;  // blocks of one tile rank on one XCD
-            const int rank = j / per, rem = j - rank * per;
-            const int pair = (rem / p.G) * 8 + x;
+            const int cb = PG * p.G * nqt;  // blocks of a full chunk of PG pairs
+            const int c = j / cb, jj = j - c * cb;
+            const int per = min(PG, ppx - c * PG) * p.G;  // blocks of one tile rank in the chunk
+            const int rank = jj / per, rem = jj - rank * per;
+            const int pair = (c * PG + rem / p.G) * 8 + x;
             a = pair / p.Hkv;
             hq = (pair - a * p.Hkv) * p.G + rem % p.G;
             qt = nqt - 1 - rank;
@@ -287,8 +302,11 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     // K and V tiles, double-buffered, filled straight from memory by LDS-DMA.
     // Chunk c of key row r sits at chunk slot c ^ swz(r) of its LDS row, so the
     // operand reads below spread over all banks without padding.
-    __shared__ __attribute__((aligned(16))) unsigned char klds[2][BN * ROW];
-    __shared__ __attribute__((aligned(16))) unsigned char vlds[2][BN * ROW];
+    // Four separate arrays, not one indexed by the buffer: accesses to distinct
+    // LDS variables are known not to alias, so the reads of one buffer need not
+    // wait for the memory-to-LDS loads into the other.
+    __shared__ __attribute__((aligned(16))) unsigned char klds0[BN * ROW], klds1[BN * ROW];
+    __shared__ __attribute__((aligned(16))) unsigned char vlds0[BN * ROW], vlds1[BN * ROW];
 
     const size_t slot = (size_t)p.Hkv * D;
     const size_t rb = (size_t)row * p.C * slot + (size_t)kv * D;
@@ -299,17 +317,19 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     // tile t into buffer buf: wave w issues DMA instructions w, w + 4, ...; lane
     // l of instruction i fetches chunk (l % CPR) ^ swz(r) of key row
     // r = RPI i + l / CPR (clamped into the prompt) into slot l % CPR
-    auto load_tile = [&](int t, int buf) {
+    auto load_tile = [&](int t, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        unsigned char *kd = buf ? klds1 : klds0, *vd = buf ? vlds1 : vlds0;
 #pragma unroll
         for (int i = w; i < NI; i += 4) {
             const int r = i * RPI + lane / CPR;
             const uint32_t off = (uint32_t)min(t * BN + r, nkeys - 1) * slotb +
                                  ((((lane % CPR) ^ swz(r)) & (CPR - 1)) << 4);
-            lds_dma16(kb + off, klds[buf] + i * 1024);
-            lds_dma16(vb + off, vlds[buf] + i * 1024);
+            lds_dma16(kb + off, kd + i * 1024);
+            lds_dma16(vb + off, vd + i * 1024);
         }
     };
-    load_tile(0, 0);
+    load_tile(0, Buf<0>{});
 
     // Per-lane byte offsets of the operand reads inside a tile; the key block,
     // the PV k-step and the buffer only add constants.
@@ -384,12 +404,12 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     auto tile = [&](const int t, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
         if (t + 1 < ntiles)
-            load_tile(t + 1, buf ^ 1);
+            load_tile(t + 1, Buf<buf ^ 1>{});
         const int k0 = t * BN;
         // some key of the tile is visible to one of this wave's queries, and the
         // wave holds at least one query of the entry
         if (k0 <= s0 + qw + 31 && qw < n) {
-            const unsigned char *kt = klds[buf], *vt = vlds[buf];
+            const unsigned char *kt = buf ? klds1 : klds0, *vt = buf ? vlds1 : vlds0;
             // two independent 32-key blocks per k-step, so each fragment read
             // overlaps the other block's product
             f32x16 st[2];
@@ -428,7 +448,11 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     tmax = fmaxf(tmax, st[b][i]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * p.scale_log2;
+            {
+                float hi = tmax;
+                swap_halves(tmax, hi);
+                tmax = fmaxf(tmax, hi) * p.scale_log2;
+            }
             const bool grow = tmax > m_run + HEADROOM;
             if (fresh) {
                 // the wave's first visible tile: key 0 is visible to every query,
@@ -487,7 +511,11 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
             tile(t + 1, Buf<1>{});
     }
 
-    l_run += __shfl_xor(l_run, 32, 64);
+    {
+        float hi = l_run;
+        swap_halves(l_run, hi);
+        l_run += hi;
+    }
     if (qrow < n) {
         const float inv = 1.0f / l_run;
         uint16_t *out = p.out + a * p.o_sa + qrow * p.o_st + hq * p.o_sh;
