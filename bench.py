@@ -86,16 +86,24 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 CSRC = os.path.join(ROOT, "positions_aware_cached_amd", "csrc")
 # the sources each kernel is built from: a counter summary stays valid for a
 # kernel while these files are unchanged
-KERNEL_SOURCES = {"decode": ("decode.hip", "kernels.h"), "prefill": ("prefill.hip", "kernels.h")}
+KERNEL_SOURCES = {"decode": ("decode.hip", "kernels.h", "elem.h"),
+                  "prefill": ("prefill.hip", "kernels.h", "elem.h")}
 
 
 def source_digest(family):
-    """Digest of one kernel family's sources ("decode" or "prefill")."""
+    """Digest of one kernel family's sources ("decode" or "prefill"): sha256
+    of the code with comments and whitespace removed, so an edit of the
+    comments alone keeps the profiler figures taken on that code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[family]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -43,7 +43,10 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds_base)
 
 // Lanes l and l ^ 32 exchange a value: v_permlane32_swap on two copies
 // leaves the low half's values in one register and the high half's in the
-// other, in every lane.
+// other, in every lane.  Inline assembly, because the compiler builtin handed
+// back one register for both results when its two inputs were the same value;
+// the s_nop gives the two wait states the instruction needs after a vector
+// write of its operands.
 __device__ __forceinline__ void swap_halves(float &a, float &b)
 {
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
