@@ -337,7 +337,9 @@ def bench_sched(args, step_ms):
     (the decode batch of the headline workload), requests of 128-512 prompt and
     64-256 new tokens arriving so that the queue never empties; row lengths are
     advanced as the prefill and decode calls would.  Timed: the boundary calls
-    only, through the Python binding (ctypes included)."""
+    only: `boundary_us` is the library call through ctypes (the plan left in
+    preallocated arrays), `with_lists_us` adds the binding's conversion of the
+    plan into Python tuples."""
     import random
 
     import torch
@@ -349,14 +351,17 @@ def bench_sched(args, step_ms):
     cache = pac.Cache.wrap([K], [torch.empty_like(K)])
     sched = pac.Scheduler(cache)
     rng = random.Random(0)
-    next_id, spent, n_adm, n_ret = 0, 0.0, 0, 0
+    next_id, spent, spent_lists, n_adm, n_ret = 0, 0.0, 0.0, 0, 0
     for i in range(args.sched_boundaries):
         while sched.counts()[0] < 8:
             sched.submit(next_id, rng.randint(128, 512), rng.randint(64, 256))
             next_id += 1
         t0 = time.perf_counter()
-        admitted, decode, retired = sched.boundary()
-        spent += time.perf_counter() - t0
+        sched.boundary_native()
+        t1 = time.perf_counter()
+        admitted, decode, retired = sched.last_plan()
+        spent += t1 - t0
+        spent_lists += time.perf_counter() - t0
         n_adm += len(admitted)
         n_ret += len(retired)
         for _, row, prompt in admitted:
@@ -365,6 +370,7 @@ def bench_sched(args, step_ms):
             cache.set_row_length(row, pos + 1)
     us = spent / args.sched_boundaries * 1e6
     return {"slots": S, "boundaries": args.sched_boundaries, "boundary_us": round(us, 2),
+            "with_lists_us": round(spent_lists / args.sched_boundaries * 1e6, 2),
             "admitted": n_adm, "retired": n_ret,
             "fraction_of_decode_step": round(us * 1e-3 / step_ms, 4)}
 

@@ -275,7 +275,16 @@ class Scheduler:
     def boundary(self):
         """One step boundary -> (admitted, decode, retired), each a list of
         (request_id, row, value) tuples (value: prompt length, position, end reason)."""
+        self.boundary_native()
+        return self.last_plan()
+
+    def boundary_native(self):
+        """The boundary call alone: the plan stays in the preallocated arrays
+        (read it with last_plan())."""
         _check(load().mllm_sched_boundary(*self._args))
+
+    def last_plan(self):
+        """The plan of the last boundary call, as boundary() returns it."""
         return tuple([(e.request_id, e.row, e.value) for e in a[:n.value]]
                      for a, n in zip(self._arrs, self._ns))
 
