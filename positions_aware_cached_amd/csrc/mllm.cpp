@@ -116,6 +116,10 @@ bool overlap(const Range &a, const Range &b)
 
 mllm_status check_aliases(const std::vector<Range> &r)
 {
+    for (const Range &x : r)
+        if (x.hi < x.lo)
+            return fail(MLLM_ERR_INVALID_ARG, "%s wraps around the end of the address space",
+                        x.name);
     for (size_t i = 0; i < r.size(); ++i)
         for (size_t j = i + 1; j < r.size(); ++j)
             if ((r[i].writable || r[j].writable) && overlap(r[i], r[j]))
@@ -164,10 +168,21 @@ mllm_status check_view(const mllm_tensor_view *v, const char *name, int ndim,
         return fail(MLLM_ERR_INVALID_ARG, "%s data pointer is null", name);
     if (((uintptr_t)v->data) % 16 != 0)
         return fail(MLLM_ERR_UNSUPPORTED, "%s data must be 16-byte aligned", name);
+    // element offset of the last element, and the bytes up to its end, with
+    // every product and sum checked (strides are the caller's)
     int64_t last = 0;
-    for (int k = 0; k < ndim; ++k)
-        last += (v->shape[k] - 1) * v->stride[k];
-    const uint64_t need = (uint64_t)(last + 1) * kElem;
+    for (int k = 0; k < ndim; ++k) {
+        int64_t term = 0;
+        if (__builtin_mul_overflow(v->shape[k] - 1, v->stride[k], &term) ||
+            __builtin_add_overflow(last, term, &last))
+            return fail(MLLM_ERR_INVALID_ARG, "%s: its shape and strides span more elements "
+                        "than a 64-bit offset holds", name);
+    }
+    uint64_t need = 0;
+    if (__builtin_mul_overflow((uint64_t)last + 1u, (uint64_t)kElem, &need) ||
+        (uintptr_t)v->data + need < (uintptr_t)v->data)
+        return fail(MLLM_ERR_INVALID_ARG, "%s: its span runs past the end of the address space",
+                    name);
     if (need > v->bytes)
         return fail(MLLM_ERR_INVALID_ARG, "%s spans %llu bytes but only %llu are accessible",
                     name, (unsigned long long)need, (unsigned long long)v->bytes);

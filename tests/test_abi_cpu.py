@@ -137,6 +137,13 @@ def test_decode_rejections_before_device():
     expect(call_decode(fc, q=fake_view([4, 4, D], FAKE + 0x1000000, nbytes=4 * 4 * D * 2 - 2)),
            "INVALID_ARG")   # view exceeds its storage
     expect(call_decode(fc, q=fake_view([4, 4, D], 0)), "INVALID_ARG")                 # null data
+    # spans that overflow a 64-bit element offset (a product, then a sum) or run
+    # past the end of the address space fail whatever bytes the view claims
+    s59 = (1 << 61) + (1 << 59)   # 3 * s59 fits, 6 * s59 does not
+    for strides in ([1 << 62, D, 1], [s59, s59, 1]):
+        expect(call_decode(fc, q=fake_view([4, 4, D], FAKE + 0x1000000, strides=strides,
+                                           nbytes=(1 << 64) - 1)), "INVALID_ARG")
+    expect(call_decode(fc, q=fake_view([4, 4, D], (1 << 64) - 1024)), "INVALID_ARG")
     expect(call_decode(fc, pos=0), "INVALID_ARG")
     # workspace
     expect(call_decode(fc, ws=0), "WORKSPACE")
@@ -219,6 +226,9 @@ def test_wrap_rejections():
     expect(L.mllm_cache_wrap(ctypes.byref(d), ks, vs, ctypes.byref(h)), "UNSUPPORTED")
     vs = (ctypes.c_void_p * 1)(0)
     expect(L.mllm_cache_wrap(ctypes.byref(d), ks, vs, ctypes.byref(h)), "INVALID_ARG")
+    vs = (ctypes.c_void_p * 1)((1 << 64) - 1024)  # the block would wrap past the top
+    expect(L.mllm_cache_wrap(ctypes.byref(d), ks, vs, ctypes.byref(h)), "INVALID_ARG")
+    assert "wraps" in pac.last_error()
 
 
 def call_prefill(fc, A=2, T=16, Hq=4, rows_host=(0, 1), ws=FAKE + 0x40000000, ws_bytes=1 << 30,
