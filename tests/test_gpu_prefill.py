@@ -113,6 +113,24 @@ def test_prefill_shapes(kernel, shape):
         assert run.cache.row_length(int(r)) == T
 
 
+@pytest.mark.parametrize("A,Hkv,G", [(6, 8, 2), (5, 16, 1)], ids=["6x8_G2", "5x16_G1"])
+def test_prefill_xcd_pair_chunks(A, Hkv, G):
+    """Entry x kv-head pair counts that fill several chunks of pairs per XCD with a
+    partial last chunk (48 pairs: 6 per XCD, chunks of 4 and 2; 80 pairs: 10 per
+    XCD, chunks 4, 4, 2): every output against the oracle, every store, the rest
+    of the cache untouched."""
+    T, D = 150, 128
+    H.log(f"prefill pair chunks A={A} Hkv={Hkv} G={G}")
+    cfg = workloads.config("prefill", A=A, S=A + 2, C=T + 10, T=T, Hq=Hkv * G, Hkv=Hkv, D=D,
+                           base=1.0e4, seed=A * Hkv + G, rows_override=list(range(A + 1, 0, -1))[:A])
+    run = PrefillRun(cfg)
+    Kpre, Vpre = run.Kc.clone(), run.Vc.clone()
+    run.run(0)
+    assert torch.isfinite(run.out.float()).all()
+    parity(run, Kpre, Vpre)
+    untouched(run, Kpre, Vpre)
+
+
 def test_prefill_full_config():
     """16 prompts x 1024 tokens, 32/8/128: every store checked, outputs of two rows
     at query positions around the tile boundaries checked against the oracle."""
