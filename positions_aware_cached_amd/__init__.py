@@ -157,6 +157,17 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _host_i32(x, n, name):
+    """A host int32 copy of exactly n values (the library reads n values through
+    the pointer, on the host): a tensor on a GPU or a wrong count is refused."""
+    if isinstance(x, torch.Tensor) and x.device.type != "cpu":
+        raise ValueError(f"{name} must be host memory, got a tensor on {x.device}")
+    t = torch.as_tensor(x, dtype=torch.int32).contiguous().reshape(-1)
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} int32 values, got {t.numel()}")
+    return t, ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -281,6 +292,8 @@ class Scheduler:
     def boundary_native(self):
         """The boundary call alone: the plan stays in the preallocated arrays
         (read it with last_plan())."""
+        if not self.cache.handle:
+            raise RuntimeError("the scheduler's cache has been freed")
         _check(load().mllm_sched_boundary(*self._args))
 
     def last_plan(self):
@@ -329,8 +342,7 @@ def decode_rope_store_attn(cache, layer, q, k_new, v_new, positions, rows, out, 
     o = _opts(waves, kernel, attn_events)
     hm = None
     if host_mirror is not None:
-        hm_t = torch.as_tensor(host_mirror, dtype=torch.int32).contiguous()
-        hm = ctypes.cast(hm_t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+        hm_t, hm = _host_i32(host_mirror, 2 * A, "host_mirror")
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().mllm_decode_rope_store_attn(
@@ -355,11 +367,10 @@ def prefill_rope_store_attn(cache, layer, q, k_new, v_new, rows_dev, rows_host, 
     A, T = q.shape[0], q.shape[1]
     rope = RopeDesc(float(base), q.shape[-1], 0)
     o = _opts(0, kernel, attn_events)
-    rh = torch.as_tensor(rows_host, dtype=torch.int32).contiguous()
+    rh, rh_p = _host_i32(rows_host, A, "rows_host")
     _check(load().mllm_prefill_rope_store_attn(
         cache.handle, layer, ctypes.byref(view(q)), ctypes.byref(view(k_new)),
-        ctypes.byref(view(v_new)), _ptr(rows_dev),
-        ctypes.cast(rh.data_ptr(), ctypes.POINTER(ctypes.c_int32)), A, T, ctypes.byref(rope),
+        ctypes.byref(view(v_new)), _ptr(rows_dev), rh_p, A, T, ctypes.byref(rope),
         ctypes.byref(view(out)), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         ctypes.byref(o), _stream(stream)))
@@ -374,13 +385,12 @@ def prefill_chunk_rope_store_attn(cache, layer, q, k_new, v_new, chunk_dev, chun
     A, T = q.shape[0], q.shape[1]
     rope = RopeDesc(float(base), q.shape[-1], 0)
     o = _opts(0, kernel, attn_events)
-    ch = torch.as_tensor(chunk_host, dtype=torch.int32).contiguous()
-    if ch.numel() != 3 * A or (chunk_dev is not None and chunk_dev.numel() != 3 * A):
+    ch, ch_p = _host_i32(chunk_host, 3 * A, "chunk_host")
+    if chunk_dev is not None and chunk_dev.numel() != 3 * A:
         raise ValueError("chunk metadata must hold 3 * A int32 values")
     _check(load().mllm_prefill_chunk_rope_store_attn(
         cache.handle, layer, ctypes.byref(view(q)), ctypes.byref(view(k_new)),
-        ctypes.byref(view(v_new)), _ptr(chunk_dev),
-        ctypes.cast(ch.data_ptr(), ctypes.POINTER(ctypes.c_int32)), A, T, ctypes.byref(rope),
+        ctypes.byref(view(v_new)), _ptr(chunk_dev), ch_p, A, T, ctypes.byref(rope),
         ctypes.byref(view(out)), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         ctypes.byref(o), _stream(stream)))
@@ -405,8 +415,7 @@ class DecodeCall:
         self.hm_t = None
         self.hm = None
         if host_mirror is not None:
-            self.hm_t = torch.as_tensor(host_mirror, dtype=torch.int32).contiguous()
-            self.hm = ctypes.cast(self.hm_t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+            self.hm_t, self.hm = _host_i32(host_mirror, 2 * self.A, "host_mirror")
         self.args_tail = (_ptr(positions), _ptr(rows), self.A, self.hm, ctypes.byref(self.rope),
                           ctypes.byref(self.vo), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _ptr(status))

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import positions_aware_cached_amd as pac
 
@@ -330,3 +331,14 @@ def test_grid_size_limits():
     big = 1 << 29
     expect(call_decode(fc, A=big, Hq=4, mirror=None), "UNSUPPORTED")
     expect(call_prefill(fc, A=2, T=256, Hq=big // 64 * 32, rows_host=(0, 1)), "UNSUPPORTED")
+
+
+def test_host_arrays_checked_by_the_binding():
+    """Host-side index arrays cross the ABI as raw host pointers that the library
+    reads for a fixed count: the binding refuses device tensors and wrong counts."""
+    t, p = pac._host_i32([1, 2, 3, 4], 4, "host_mirror")
+    assert t.dtype == torch.int32 and [p[i] for i in range(4)] == [1, 2, 3, 4]
+    with pytest.raises(ValueError, match="hold 4"):
+        pac._host_i32([1, 2, 3], 4, "host_mirror")
+    with pytest.raises(ValueError, match="host memory"):
+        pac._host_i32(torch.empty(4, dtype=torch.int32, device="meta"), 4, "rows_host")

@@ -118,6 +118,15 @@ def test_cancel_queued_and_errors():
     assert s.counts() == (1, 1)
 
 
+def test_boundary_refused_after_cache_free():
+    fc = FakeCache(S=2, C=16)
+    s = pac.Scheduler(fc.cache)
+    s.submit(1, 4, 2)
+    fc.cache.free()
+    with pytest.raises(RuntimeError):
+        s.boundary()
+
+
 def test_create_rules():
     fc = FakeCache(S=2, C=16)
     with pytest.raises(pac.MllmError) as e:
