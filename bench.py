@@ -85,7 +85,7 @@ def percentile(xs, q):
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 CSRC = os.path.join(ROOT, "positions_aware_cached_amd", "csrc")
 # the sources each kernel is built from: a counter summary stays valid for a
-# kernel while these files are unchanged
+# kernel while their code (comments and whitespace aside) is unchanged
 KERNEL_SOURCES = {"decode": ("decode.hip", "kernels.h", "elem.h"),
                   "prefill": ("prefill.hip", "kernels.h", "elem.h")}
 
