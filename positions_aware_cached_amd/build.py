@@ -7,6 +7,7 @@ with fast-math or denormal flushing.
 """
 import glob
 import os
+import shutil
 import subprocess
 import sys
 import tempfile
@@ -29,6 +30,13 @@ def build(out=LIB, verbose=False, jobs=8):
     """Compile every source (in parallel) and link out; returns out."""
     srcs = sources()
     tmpdir = tempfile.mkdtemp(prefix="mllm_build_")
+    try:
+        return _build_in(srcs, tmpdir, out, verbose, jobs)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
+
+
+def _build_in(srcs, tmpdir, out, verbose, jobs):
     procs, objs = [], []
     for s in srcs:
         obj = os.path.join(tmpdir, os.path.basename(s) + ".o")
