@@ -235,9 +235,11 @@ struct Buf {
 //   O^T += V^T P^T on the same instruction: the score registers are already
 //       the B operand (16 keys per k-step, in the key order above) and V^T is
 //       read from the row-major LDS tile with ds_read_b64_tr_b16 in that order.
-// The rotated query and the weights enter the matrix cores in the storage
-// type (rounded to nearest even); products accumulate in FP32; the output is
-// rounded once.
+// The FP32 rotated query enters the matrix cores as two parts in the storage
+// type (the high part and the rounded remainder: 2^-16 relative for BF16,
+// 2^-22 for FP16), so the scores keep their accuracy at any magnitude; the
+// weights (in [0, 1]) are rounded once to nearest even; products accumulate
+// in FP32; the output is rounded once.
 template <class E, int D>
 __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const float2 *table)
 {
@@ -355,8 +357,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
         }
     }
 
-    // B operands of QK: the rotated query of this lane's row, dims 16 ks + 8 hh + j
-    vec8 bq[KS];
+    // B operands of QK: the rotated query of this lane's row, dims 16 ks + 8 hh + j,
+    // as two parts in the storage type (high part and rounded remainder)
+    vec8 bq[2][KS];
     {
         const int tq = min(qrow, n - 1);
         const uint16_t *qs = p.q + a * p.q_sa + tq * p.q_st + hq * p.q_sh;
@@ -382,13 +385,16 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                 x[ks + KS / 2][j] = hi;
             }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 v;
+        for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = E::pack2(x[ks][2 * e], x[ks][2 * e + 1]);
-            bq[ks] = __builtin_bit_cast(vec8, v);
-        }
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = E::template part<2>(x[ks][2 * e], pp) |
+                           (E::template part<2>(x[ks][2 * e + 1], pp) << 16);
+                bq[pp][ks] = __builtin_bit_cast(vec8, v);
+            }
     }
 
     f32x16 O[NDB];
@@ -428,8 +434,10 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                 for (int b = 0; b < 2; ++b)
                     kf[b] = *(const u32x4 *)(kt + koff[ks] + b * 32 * ROW);
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    st[b] = E::mma32(__builtin_bit_cast(vec8, kf[b]), bq[ks], st[b]);
+                for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        st[b] = E::mma32(__builtin_bit_cast(vec8, kf[b]), bq[pp][ks], st[b]);
             }
             // raw scores; the scale (> 0) is applied inside exp2 below, so the max
             // is taken on the raw values.  Only tiles that reach past the first
