@@ -11,7 +11,7 @@
 // page's equal-length prefill into empty rows.
 //
 //   k_prefill_store     one wave per (token t, entry a): split-half RoPE of
-//                       k_new -> store in the storage type, v_new bit copy; the block also
+//                       k_new -> store in the storage type, v_new bit copy; the wave also
 //                       writes the FP32 cos/sin table row of (a, t).
 //   k_prefill_mfma      the tuned attention: one workgroup of four waves per
 //                       (entry, query head, 128-query tile), FlashAttention-
@@ -225,8 +225,9 @@ struct Buf {
 //
 // One workgroup (4 waves, wave w owns queries q0 + 32 w .. + 31) per (entry a,
 // query head hq, query tile q0 .. q0 + 127); the kv head is hq / G.  Key tiles
-// of 64 are staged through two padded LDS buffers (the next tile is loaded
-// into registers while the current one is computed).  Per tile and wave:
+// of 64 move from memory straight into two LDS buffers by LDS-DMA (the next
+// tile while the current one is computed), each key row's 16-byte chunks
+// permuted by swz.  Per tile and wave:
 //   S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16} (A = 32 keys x 16 dims of K, B =
 //       16 dims x 32 queries of the rotated query): lane l owns query l % 32
 //       and keys 8 (i / 4) + 4 (l / 32) + i % 4 (i < 16) of each 32-key block,
