@@ -5,11 +5,13 @@
 // store and cached attention; rows not named in cache_rows stay untouched.
 //
 // Tuned path, two launches on one stream:
-//   k_decode_stream   NW resident waves split the keys of all (entry, kv head)
+//   k_decode_stream   NW resident work groups (one wave per kv head of a head
+//                     group) split the keys of all (entry, head group)
 //                     segments evenly: RoPE of the queries, RoPE(K) + K/V store
-//                     by the wave that holds a segment's last tile, scores and
+//                     by the group that holds a segment's last tile, scores and
 //                     P.V on the matrix cores, online FP32 softmax, one partial
-//                     (max, sum, unnormalized output) per segment and wave;
+//                     (max, sum, unnormalized output) per segment, group and
+//                     query head;
 //   k_decode_merge    one wave per (entry, query head): rescales and sums the
 //                     partials of its segment (the streaming-attention merge
 //                     of the IPU refactor log, "Flash vs materialized
