@@ -38,11 +38,12 @@ def _scaled(x, c):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("D", [64, 128])
-def test_decode_growing_and_shrinking_scores(dtype, D):
+@pytest.mark.parametrize("D,G", [(64, 4), (128, 4), (128, 8), (64, 16)])
+def test_decode_growing_and_shrinking_scores(dtype, D, G):
+    """G <= 4 carries the BF16 query exactly in three parts, larger groups in two."""
     A, Cap = 6, 600
-    H.log(f"decode score range D={D} {dtype}")
-    cfg = workloads.config("tiny", A=A, S=A + 1, C=Cap, Hq=8, Hkv=2, D=D, seed=61 + D,
+    H.log(f"decode score range D={D} G={G} {dtype}")
+    cfg = workloads.config("tiny", A=A, S=A + 1, C=Cap, Hq=2 * G, Hkv=2, D=D, seed=61 + D + G,
                            rows="subset", dtype=dtype)
     inp = workloads.draw_decode(cfg, device="cpu")
     pos = np.array([599, 300, 257, 64, 500, 33], dtype=np.int32)
