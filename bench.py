@@ -90,7 +90,7 @@ KERNEL_SOURCES = {"decode": ("decode.hip", "kernels.h", "elem.h"),
                   "prefill": ("prefill.hip", "kernels.h", "elem.h")}
 
 
-def source_digest(family):
+def source_digest(family, csrc=CSRC):
     """Digest of one kernel family's sources ("decode" or "prefill"): sha256
     of the code with comments and whitespace removed, so an edit of the
     comments alone keeps the profiler figures taken on that code."""
@@ -98,7 +98,7 @@ def source_digest(family):
     import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[family]:
-        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
