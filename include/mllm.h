@@ -238,9 +238,10 @@ mllm_status mllm_prefill_workspace_size(const mllm_cache *cache, int32_t A, int3
  *   K[r, t, h, :] = rnd(RoPE(k_new[a, t, h, :], t)), V[r, t, h, :] = v_new[a, t, h, :];
  *   out[a, t, hq, :] = causal GQA attention of RoPE(q[a, t, hq], t) over keys
  *   0..t of row r, FP32 softmax, output rounded to the storage type.  The
- *   attention products run on the matrix cores in the storage type: the
- *   rotated query and the softmax weights are rounded to it before each
- *   product, accumulation is FP32.
+ *   attention products run on the matrix cores in the storage type: the FP32
+ *   rotated query enters as two parts (high part and rounded remainder:
+ *   2^-16 relative for BF16, 2^-22 for FP16), the softmax weights (in [0, 1])
+ *   are rounded to the storage type once, accumulation is FP32.
  * Positions >= T of row r and every other row stay untouched.
  *
  *  cache_rows_dev  : device int32[A]; cache_rows_host: host int32[A], the
