@@ -10,5 +10,5 @@ if HERE not in sys.path:
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; run on the GPU box")
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long-running CPU test")
