@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
     MLLM_OK = 0,
     MLLM_ERR_INVALID_ARG = 1,  /* null pointer, bad shape/stride/size, out-of-range index */
-    MLLM_ERR_UNSUPPORTED = 2,  /* dtype, head size or layout this build does not handle */
+    MLLM_ERR_UNSUPPORTED = 2,  /* dtype, head size or layout the library does not handle */
     MLLM_ERR_ALIAS = 3,        /* a writable buffer overlaps another argument */
     MLLM_ERR_OUT_OF_RANGE = 4, /* position or row outside the cache (host mirror check) */
     MLLM_ERR_ROW_BUSY = 5,     /* prefill target row is not logically empty */
@@ -166,8 +166,8 @@ mllm_status mllm_cache_set_row_length(mllm_cache *cache, int32_t row, int32_t le
 
 /* Workspace bytes needed by mllm_decode_rope_store_attn for A entries and h_q
  * query heads with the given opts (may be NULL).  max_position bounds every
- * position of the call (-1 = capacity - 1); this build's size does not depend
- * on it.  The size is the same for every position, so one workspace serves
+ * position of the call (-1 = capacity - 1); the current layout's size does not
+ * depend on it.  The size is the same for every position, so one workspace serves
  * every step of a decode loop. */
 mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32_t h_q,
                                        int32_t max_position, const mllm_decode_opts *opts,
