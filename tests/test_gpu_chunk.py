@@ -238,3 +238,46 @@ def test_chunk_full_config():
     ref = np.concatenate([slow[a, :lens[a]] for a in range(cfg["A"])])
     H.check_output(got, ref, "mfma vs readable (every written output)")
     assert (fast == slow)[np.arange(fast.shape[1])[None, :] >= lens[:, None]].all()
+
+
+@pytest.mark.parametrize("kernel", [0, 1], ids=["mfma", "readable"])
+def test_chunk_graph_capture_replay(kernel):
+    """A prefill chunk captured into a HIP graph (the call allocates and memsets
+    nothing) replays to the eager result, stores and output bit for bit, on
+    every replay, with eager work and synchronizations in between."""
+    T, Hq, Hkv, D = 96, 8, 2, 128
+    starts, lens, rows = [0, 40, 130, 7], [96, 57, 1, 80], [5, 0, 3, 1]
+    H.log(f"chunk graph capture kernel={kernel}")
+    cfg = _case_cfg(T, Hq, Hkv, D, starts, lens, seed=41)
+    run = ChunkRun(cfg, starts, lens, rows)
+    Kpre, Vpre = run.Kc.clone(), run.Vc.clone()
+    want = run.run(kernel).clone()
+    Kw, Vw = run.Kc.clone(), run.Vc.clone()
+    parity(run, Kpre, Vpre)
+    A = run.q.shape[0]
+    ws = torch.empty(max(256, pac.prefill_workspace_size(run.cache, A, T, Hq)), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        pac.prefill_chunk_rope_store_attn(run.cache, 0, run.q, run.k, run.v, run.meta,
+                                          run.meta_h, run.out, ws, cfg["base"], kernel=kernel)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on the capture stream
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        run.out.view(torch.int16).fill_(int(SENT))
+        run.Kc.copy_(Kpre)
+        run.Vc.copy_(Vpre)
+        ws.fill_(0x5A)  # the workspace carries nothing from one call to the next
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(run.out.view(torch.int16), want.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(run.Kc.view(torch.int16), Kw.view(torch.int16)), f"replay {rep} K"
+        assert torch.equal(run.Vc.view(torch.int16), Vw.view(torch.int16)), f"replay {rep} V"
