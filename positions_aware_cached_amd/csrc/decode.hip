@@ -185,7 +185,8 @@ __device__ __forceinline__ float wave_max(float v)
 // where n(a) is entry a's tile count (0 for an entry whose position or row is
 // out of range) and E(a) = n(0) + ... + n(a - 1).  Wave w owns the global
 // tiles [t0(w), t0(w + 1)), t0(w) = floor(w NT / NW): every wave gets the same
-// number of tiles whatever the row lengths, so all finish together.  A wave
+// number of tiles whatever the row lengths (with two groups per compute unit
+// the first-dispatched half gets a larger share, see plan_t0).  A wave
 // walks its range across segment boundaries, keeps the next tile in flight
 // across them, and writes one partial (reference max, sum, unnormalized
 // output of each of the G query heads) per segment it touches into slot
@@ -333,17 +334,54 @@ __device__ void plan_locate(const DecodeParams &p, long long t, int lane, int &a
     e_pos = e_row = e_na = 0;
 }
 
-// Groups of the plan: min(launched, NT); then group w owns tiles
-// [floor(w NT / NW), floor((w + 1) NT / NW)), never an empty range.
+// Groups of the plan: min(launched, NT); group w owns the tiles
+// [t0(w), t0(w + 1)) (below), never an empty range.
 __device__ __forceinline__ int plan_waves(int launched, long long NT)
 {
     return (int)min((long long)launched, NT);
 }
 
-// Group that owns global tile t (inverse of t0(w) = floor(w NT / NW)).
-__device__ __forceinline__ int plan_wave_of(long long t, long long NT, int NW)
+// First tile of group w.  With two resident groups per compute unit the
+// groups of the first half are each unit's first-dispatched group, whose waves
+// win the instruction-issue ties of their SIMDs and run ahead (measured on
+// MI355X: with equal shares the second half finished 12-13 % later, on every
+// batch shape).  When the segments are long (at least 32 tiles each on
+// average), a group's time follows its tile count, and the first half gets
+// weight kWA, the second kWB: t0(w) = floor(W(w) NT / W(NW)), W the running
+// weight.  With short segments the per-segment work dominates and the tile
+// weights measured slower, so the split stays uniform (weight 1 each), as it
+// does when NW is odd or there are fewer than four tiles per group (no range
+// is empty).
+constexpr long long kWA = 18, kWB = 14;
+__device__ __forceinline__ bool plan_is_weighted(const DecodeParams &p, long long NT, int NW)
 {
-    return (int)(((t + 1) * NW - 1) / NT);
+    return p.plan_weighted && !(NW & 1) && NT >= 4ll * NW &&
+           NT >= 32ll * p.A * p.NHG;
+}
+__device__ __forceinline__ long long plan_weight(int w, bool weighted, int NW)
+{
+    if (!weighted)
+        return w;
+    const long long C = NW >> 1;
+    return w <= C ? kWA * w : kWA * C + kWB * (w - C);
+}
+__device__ __forceinline__ long long plan_t0(const DecodeParams &p, int w, long long NT, int NW)
+{
+    const bool wt = plan_is_weighted(p, NT, NW);
+    return plan_weight(w, wt, NW) * NT / plan_weight(NW, wt, NW);
+}
+
+// Group that owns global tile t: the largest w with t0(w) <= t, i.e. with
+// W(w) <= X = floor(((t + 1) W(NW) - 1) / NT).
+__device__ __forceinline__ int plan_wave_of(const DecodeParams &p, long long t, long long NT, int NW)
+{
+    const bool wt = plan_is_weighted(p, NT, NW);
+    const long long X = ((t + 1) * plan_weight(NW, wt, NW) - 1) / NT;
+    if (!wt)
+        return (int)X;
+    const int C = NW >> 1;
+    const long long w = X <= kWA * C ? X / kWA : C + (X - kWA * C) / kWB;
+    return (int)min(w, (long long)NW - 1);
 }
 
 // LDS of one wave: K tile, padded V tile, new key / value (rotated and raw),
@@ -409,7 +447,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     }
     if (w >= NW)
         return;
-    const long long t0 = (long long)w * NT / NW, t1 = (long long)(w + 1) * NT / NW;
+    const long long t0 = plan_t0(p, w, NT, NW), t1 = plan_t0(p, w + 1, NT, NW);
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     using L = WaveLds<D, GCLS>;
@@ -825,7 +863,7 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
     const int NW = plan_waves(p.NS, NT);      // NT >= 1: this entry is valid
     const int na = (pos + kTile) / kTile;
     const long long ts = before + (long long)hg * na;
-    const int wf = plan_wave_of(ts, NT, NW), wl = plan_wave_of(ts + na - 1, NT, NW);
+    const int wf = plan_wave_of(p, ts, NT, NW), wl = plan_wave_of(p, ts + na - 1, NT, NW);
     const int ns = wl - wf + 1;
     // partial of group wf + x for this head: (max, sum) and D outputs
     auto slot_of = [&](int x) { return ((size_t)(a * NHG + hg + wf + x) * HG + wi) * G + g; };

@@ -29,6 +29,8 @@ struct DecodeParams {
     int32_t dtype;     // storage type of every 16-bit tensor: 1 BF16, 2 FP16
     int32_t A, S, C, Hq, Hkv, D, G;
     int32_t NS;        // work groups of the decode launch
+    int32_t plan_weighted;  // 1: the launch holds two resident groups per compute unit
+                            // (the first-dispatched half gets more tiles, see plan_t0)
     int32_t HG, NHG;   // kv heads per group (one wave each), head groups per entry
     float scale_log2;  // log2(e) / sqrt(D)
     float inv_freq[kMaxHalfDim];

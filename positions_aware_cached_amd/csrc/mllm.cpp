@@ -252,6 +252,22 @@ int launch_groups(int requested_waves, int device, int D, int G, int hg, int dty
     return ng;
 }
 
+// Compute units of a device (queried once per device).
+int device_cus(int device)
+{
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(device);
+    if (it != cache.end())
+        return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        cus = 0;
+    cache[device] = cus;
+    return cus;
+}
+
 mllm_status check_device_current(int device)
 {
     int cur = -1;
@@ -580,6 +596,9 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     p.HG = mllm::decode_head_group(d.h_kv, G);
     p.NHG = d.h_kv / p.HG;
     p.NS = launch_groups(waves, d.device, D, G, p.HG, d.dtype);
+    // the device's resident groups, two per compute unit: the plan gives the
+    // first-dispatched half a larger share (see the decode kernel's plan)
+    p.plan_weighted = waves == 0 && p.NS == 2 * device_cus(d.device) ? 1 : 0;
     p.dtype = d.dtype;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     fill_inv_freq(p.inv_freq, rope->base, D);
