@@ -225,6 +225,31 @@ struct Cols {
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
+// v rotated by K lanes within each row of 16 lanes (DPP row_ror: VALU only)
+template <int K>
+__device__ __forceinline__ float row_ror(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + K, 0xf, 0xf, false));
+}
+
+// Sum of v over the lanes of this lane's 16-lane row that share lane % GS
+// (one operand column class: the parts of one head).  A rotation tree, so
+// every lane of a class ends with the same bits.
+template <int GS>
+__device__ __forceinline__ float class_sum(float v)
+{
+    if constexpr (GS <= 8)
+        v += row_ror<8>(v);
+    if constexpr (GS <= 4)
+        v += row_ror<4>(v);
+    if constexpr (GS <= 2)
+        v += row_ror<2>(v);
+    if constexpr (GS <= 1)
+        v += row_ror<1>(v);
+    return v;
+}
+
 // 2^x for x <= HEADROOM or -inf (the softmax weights): the hardware exp2.
 // Its result for arguments below -126 is flushed to zero, which only drops
 // weights under 2^-126 of the running maximum.
@@ -673,10 +698,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             for (int i = 0; i < 4; ++i) {
                 float v;
                 if (NGRP == 1) {
-                    v = 0.0f;
-#pragma unroll
-                    for (int q = 0; q < NPART; ++q)
-                        v += __shfl(O[0][db][i], lg * 16 + min(n + q * GS, 15), 64);
+                    v = class_sum<GS>(ccol ? O[0][db][i] : 0.0f);
                 } else {
                     v = O[0][db][i] + O[1][db][i];
                 }
@@ -711,6 +733,11 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
                 fetch_segment(nxa, nxh, nxbase, nxna);
             load_tile(seg_base(nxrow, nxh, p.kc), seg_base(nxrow, nxh, p.vc), nxj * TK,
                       nxpos + 1);
+            // cos/sin of a segment that starts at the next tile, while the
+            // loads are in flight (the last reads of cs/sn were fenced by the
+            // barrier that ended the previous iteration)
+            if (nxj == 0)
+                angles(nxa, nxpos);
         }
         const bool seg_ends = !more || nxj == 0;
         const int jt = j * TK;
@@ -723,14 +750,23 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             for (int c = 0; c < NGRP; ++c)
                 acc[b][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
+            u32x4 kf[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 kf = *(const u32x4 *)(klds + (b * KS + ks) * 1024 + lane * 16);
+            for (int ks = 0; ks < KS; ++ks)
+                kf[ks] = *(const u32x4 *)(klds + (b * KS + ks) * 1024 + lane * 16);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int c = 0; c < NGRP; ++c)
-                    acc[b][c] = E::mma16(__builtin_bit_cast(vec8, kf), bq[c][ks], acc[b][c]);
-            }
+                    acc[b][c] = E::mma16(__builtin_bit_cast(vec8, kf[ks]), bq[c][ks], acc[b][c]);
+        }
+        // the scheduler keeps each block's fragment reads together, ahead of its products
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, KS * NGRP, 0);
+        }
         float sc[NB][4];
         float tmax = -INFINITY;
 #pragma unroll
@@ -739,10 +775,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             for (int i = 0; i < 4; ++i) {
                 float v;
                 if (NGRP == 1) {
-                    v = 0.0f;
-#pragma unroll
-                    for (int q = 0; q < NPART; ++q)
-                        v += __shfl(acc[b][0][i], lg * 16 + min(chead + q * GS, 15), 64);
+                    v = class_sum<GS>(ccol ? acc[b][0][i] : 0.0f);
                 } else {
                     v = acc[b][0][i] + acc[b][1][i];
                 }
@@ -801,9 +834,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             for (int c = 0; c < NGRP; ++c)
                 O[c][db] = E::mma16(vt, pb[c], O[c][db]);
         }
-        if (more && seg_ends)
-            angles(nxa, nxpos);  // overlaps the loads in flight
-        __syncthreads();         // LDS of tile t fully read
+        __syncthreads();  // LDS of tile t fully read
 
         // the one wait per tile: tile t+1 (and the segment inputs issued
         // before it) into LDS; then this segment's partial and the next
