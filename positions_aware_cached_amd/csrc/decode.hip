@@ -263,23 +263,26 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds_base)
                                      (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
-__device__ __forceinline__ long long wave_sum_ll(long long v)
+// v shifted up by K lanes within each row of 16 lanes, 0 in the row's first K
+// lanes (DPP row_shr)
+template <int K>
+__device__ __forceinline__ int row_shr_zero(int v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
+    return __builtin_amdgcn_update_dpp(0, v, 0x110 + K, 0xf, 0xf, false);
 }
 
+// Inclusive prefix sum over the 64 lanes: a shift-and-add tree within each
+// 16-lane row, then the totals of the rows below (lanes 15, 31, 47).
 __device__ __forceinline__ int wave_incl_scan(int v, int lane)
 {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(v, o, 64);
-        if (lane >= o)
-            v += t;
-    }
-    return v;
+    v += row_shr_zero<1>(v);
+    v += row_shr_zero<2>(v);
+    v += row_shr_zero<4>(v);
+    v += row_shr_zero<8>(v);
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+              r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // Tile count of entry x from its position and row: 0 when x >= A or the entry
@@ -309,35 +312,56 @@ __device__ __forceinline__ void load_block(const DecodeParams &p, int c0, int la
         b.na[k] = tiles_of(p, c0 + 64 * k + lane, b.pos[k], b.row[k]);
 }
 
-// NT = NHG * sum_a n(a) and NHG * sum_{x < a} n(x), on every lane.
-__device__ void plan_sums(const DecodeParams &p, int a, int lane, long long &NT, long long &before)
+// A block of entries with the inclusive scans of its tile counts: incl[k] on
+// lane l sums n(c0 + 64 k + i) for i <= l.
+struct ScanBlock {
+    EntryBlock b;
+    int incl[4];
+};
+__device__ __forceinline__ void scan_block(const DecodeParams &p, int c0, int lane, ScanBlock &s)
 {
-    long long s = 0, sb = 0;
-    for (int c0 = 0; c0 < p.A; c0 += 256) {
-        EntryBlock b;
-        load_block(p, c0, lane, b);
+    load_block(p, c0, lane, s.b);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            s += b.na[k];
-            sb += c0 + 64 * k + lane < a ? b.na[k] : 0;
-        }
+    for (int k = 0; k < 4; ++k)
+        s.incl[k] = wave_incl_scan(s.b.na[k], lane);
+}
+
+// NT = NHG * sum_a n(a), on every lane; the first block (entries 0..255) is
+// left in first, so that the plan's later passes need not read it again.
+__device__ long long plan_total(const DecodeParams &p, int lane, ScanBlock &first)
+{
+    scan_block(p, 0, lane, first);
+    long long s = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        s += __builtin_amdgcn_readlane(first.incl[k], 63);
+    for (int c0 = 256; c0 < p.A; c0 += 256) {
+        ScanBlock sb;
+        scan_block(p, c0, lane, sb);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            s += __builtin_amdgcn_readlane(sb.incl[k], 63);
     }
-    NT = wave_sum_ll(s) * p.NHG;
-    before = wave_sum_ll(sb) * p.NHG;
+    return s * p.NHG;
 }
 
 // The entry holding global tile t < NT, NHG * E(entry), and the 64-entry chunk
 // around it (lane l: entry ec + l), on every lane.
-__device__ void plan_locate(const DecodeParams &p, long long t, int lane, int &a_out,
-                            long long &base_out, int &ec, int &e_pos, int &e_row, int &e_na)
+__device__ void plan_locate(const DecodeParams &p, long long t, int lane, const ScanBlock &first,
+                            int &a_out, long long &base_out, int &ec, int &e_pos, int &e_row,
+                            int &e_na)
 {
     long long run = 0;
     for (int c0 = 0; c0 < p.A; c0 += 256) {
-        EntryBlock b;
-        load_block(p, c0, lane, b);
+        ScanBlock sb;
+        if (c0 == 0)
+            sb = first;
+        else
+            scan_block(p, c0, lane, sb);
+        const EntryBlock &b = sb.b;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int incl = wave_incl_scan(b.na[k], lane);
+            const int incl = sb.incl[k];
             const long long end = run + (long long)p.NHG * incl;
             const unsigned long long hit = __ballot(t < end && b.na[k] > 0);
             if (hit) {
@@ -350,7 +374,7 @@ __device__ void plan_locate(const DecodeParams &p, long long t, int lane, int &a
                 e_na = b.na[k];
                 return;
             }
-            run += (long long)p.NHG * __shfl(incl, 63, 64);
+            run += (long long)p.NHG * __builtin_amdgcn_readlane(incl, 63);
         }
     }
     a_out = p.A;  // not reached for t < NT
@@ -449,22 +473,24 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     const float my_freq = p.inv_freq[lane & (D / 2 - 1)];
 
     // the plan uses min(launched groups, NT) groups, so each owns at least one tile
-    long long NT, unused;
-    plan_sums(p, 0, lane, NT, unused);
+    ScanBlock first;
+    const long long NT = plan_total(p, lane, first);
     const int NW = plan_waves(p.NS, NT);
     if (w == 0 && wi == 0) {
         // the plan's prefix for the merge kernel: tiles before each entry, then NT
         long long run = 0;
         for (int c0 = 0; c0 < p.A; c0 += 256) {
-            EntryBlock b;
-            load_block(p, c0, lane, b);
+            ScanBlock sb;
+            if (c0 == 0)
+                sb = first;
+            else
+                scan_block(p, c0, lane, sb);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int incl = wave_incl_scan(b.na[k], lane);
                 const int x = c0 + 64 * k + lane;
                 if (x < p.A)
-                    p.plan[x] = run + (long long)NHG * (incl - b.na[k]);
-                run += (long long)NHG * __shfl(incl, 63, 64);
+                    p.plan[x] = run + (long long)NHG * (sb.incl[k] - sb.b.na[k]);
+                run += (long long)NHG * __builtin_amdgcn_readlane(sb.incl[k], 63);
             }
         }
         if (lane == 0)
@@ -494,7 +520,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     int ec, e_pos, e_row, e_na;
     int a, h, j, na, row, pos;
     long long ebase;
-    plan_locate(p, t0, lane, a, ebase, ec, e_pos, e_row, e_na);
+    plan_locate(p, t0, lane, first, a, ebase, ec, e_pos, e_row, e_na);
     auto entry = [&](int e, int &pos_o, int &row_o, int &na_o) {
         if (e < ec || e >= ec + 64) {  // wave-uniform; once per 64 entries
             ec = e & ~63;
