@@ -397,11 +397,12 @@ __device__ __forceinline__ int plan_waves(int launched, long long NT)
 // batch shape).  When the segments are long (at least 32 tiles each on
 // average), a group's time follows its tile count, and the first half gets
 // weight kWA, the second kWB: t0(w) = floor(W(w) NT / W(NW)), W the running
-// weight.  With short segments the per-segment work dominates and the tile
+// weight (37 : 27, the best of the ratios 1.29, 1.32, 1.37, 1.43, 1.5 and 1.6
+// measured on the Llama-like and long-context batches).  With short segments the per-segment work dominates and the tile
 // weights measured slower, so the split stays uniform (weight 1 each), as it
 // does when NW is odd or there are fewer than four tiles per group (no range
 // is empty).
-constexpr long long kWA = 18, kWB = 14;
+constexpr long long kWA = 37, kWB = 27;
 __device__ __forceinline__ bool plan_is_weighted(const DecodeParams &p, long long NT, int NW)
 {
     return p.plan_weighted && !(NW & 1) && NT >= 4ll * NW &&
