@@ -398,10 +398,10 @@ __device__ __forceinline__ int plan_waves(int launched, long long NT)
 // average), a group's time follows its tile count, and the first half gets
 // weight kWA, the second kWB: t0(w) = floor(W(w) NT / W(NW)), W the running
 // weight (37 : 27, the best of the ratios 1.29, 1.32, 1.37, 1.43, 1.5 and 1.6
-// measured on the Llama-like and long-context batches).  With short segments the per-segment work dominates and the tile
-// weights measured slower, so the split stays uniform (weight 1 each), as it
-// does when NW is odd or there are fewer than four tiles per group (no range
-// is empty).
+// measured on the Llama-like and long-context batches).  With short segments
+// the per-segment work dominates and the tile weights measured no faster, so
+// the split stays uniform (weight 1 each), as it does when NW is odd or there
+// are fewer than four tiles per group (no range is empty).
 constexpr long long kWA = 37, kWB = 27;
 __device__ __forceinline__ bool plan_is_weighted(const DecodeParams &p, long long NT, int NW)
 {
