@@ -2,8 +2,9 @@
 
 Bar: V store and untouched cache bytes bit-exact, rotated K store within one
 BF16 ulp, BF16 output within max-abs 2e-2 and RMS 4e-3.  The matrix-core
-kernel rounds the rotated query and the softmax weights to BF16 before its
-products (FP32 accumulation); the bar applies unchanged.
+kernel carries the FP32 rotated query as two parts in the storage type (the
+high part and the rounded remainder) and rounds the softmax weights once
+before its products (FP32 accumulation); the bar applies unchanged.
 """
 import numpy as np
 import pytest
