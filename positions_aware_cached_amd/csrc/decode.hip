@@ -985,6 +985,113 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
         out[lane + 64 * e] = (uint16_t)E::from_f(O[e] / L);
 }
 
+// ---------------------------------------------------------------- R4 (wide)
+// The same merge for rows split over many groups (small batches, fan-in of
+// tens to hundreds): per batch of up to 64 groups their (max, sum) pairs and
+// every lane's PER consecutive output dims (one vector load per group, at a
+// constant stride from one base), so a fan-in of 100 takes two trips where
+// the kernel above takes seven.
+template <class E, int D>
+__global__ __launch_bounds__(64) void k_decode_merge_wide(DecodeParams p)
+{
+    constexpr int B = 64, CH = 8;  // groups per round trip, per load chunk
+    constexpr int PER = D / 64;  // lane l owns the output dims PER l .. PER l + PER - 1
+    // one-dimensional grid of A * Hq waves (the y and z grid sizes are limited)
+    const int hq = (int)(blockIdx.x % (unsigned)p.Hq), a = (int)(blockIdx.x / (unsigned)p.Hq);
+    const int lane = threadIdx.x;
+    const int pos = p.positions[a], row = p.rows[a];
+    const long long before = p.plan[a], NT = p.plan[p.A];
+    uint16_t *out = p.out + a * p.o_sa + hq * p.o_sh + lane * PER;
+    if (!entry_valid(p, pos, row)) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            out[e] = E::qnan;
+        if (hq == 0 && lane == 0 && p.status)
+            p.status[0] = 1;
+        return;
+    }
+    const int G = p.G, h = hq / G, g = hq - h * G, HG = p.HG, NHG = p.NHG;
+    const int hg = h / HG, wi = h - hg * HG;  // head group, wave of the group
+    const int NW = plan_waves(p.NS, NT);      // NT >= 1: this entry is valid
+    const int na = (pos + kTile) / kTile;
+    const long long ts = before + (long long)hg * na;
+    const int wf = plan_wave_of(p, ts, NT, NW), wl = plan_wave_of(p, ts + na - 1, NT, NW);
+    const int ns = wl - wf + 1;
+    // the partial of group wf + x for this head sits in slot slot0 + x * step:
+    // (max, sum) pairs step apart, outputs step * D floats apart (at most
+    // 8 * 16 * 128 * 4 B, so 64 of them span less than 2^32 bytes)
+    const size_t slot0 = ((size_t)(a * NHG + hg + wf) * HG + wi) * G + g;
+    const size_t step = (size_t)HG * G;
+    const float2 *ml_base = (const float2 *)p.part_ml + slot0;
+    const unsigned char *o_base = (const unsigned char *)(p.part_o + slot0 * D);
+    const uint32_t o_step = (uint32_t)(step * D * 4), o_lane = (uint32_t)(lane * PER * 4);
+    float lw = 0.0f, O[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+        O[e] = 0.0f;
+    float M = -INFINITY;
+    // batches of up to B groups, each in one round trip: lane u loads the
+    // (max, sum) of group c + u, and every lane its dims of every output
+    for (int c = 0; c < ns; c += B) {
+        float m_u = -INFINITY, l_u = 0.0f;
+        if (c + lane < ns) {
+            const float2 ml = ml_base[(size_t)(c + lane) * step];
+            m_u = ml.x;
+            l_u = ml.y;
+        }
+        const int cnt = min(B, ns - c);
+        const unsigned char *ob = o_base + (size_t)c * o_step;
+        // outputs in chunks of CH groups; within a started chunk, groups past
+        // cnt re-read group cnt - 1 (in bounds, finite) and get weight 0
+        float x[B][PER];
+#pragma unroll
+        for (int k = 0; k < B; k += CH) {
+            if (k < cnt) {
+#pragma unroll
+                for (int u = k; u < k + CH; ++u) {
+                    const unsigned char *src = ob + (uint32_t)min(u, cnt - 1) * o_step + o_lane;
+                    if constexpr (PER == 2) {
+                        const float2 v = *(const float2 *)src;
+                        x[u][0] = v.x;
+                        x[u][1] = v.y;
+                    } else {
+                        x[u][0] = *(const float *)src;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int u = k; u < k + CH; ++u)
+#pragma unroll
+                    for (int e = 0; e < PER; ++e)
+                        x[u][e] = 0.0f;
+            }
+        }
+        // rescale what earlier batches summed to the new maximum
+        const float m_new = fmaxf(M, wave_max(m_u));
+        const float alpha = exp2f(M - m_new);  // 0 on the first batch (M = -inf)
+        lw *= alpha;
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            O[e] *= alpha;
+        M = m_new;
+        const float wgt = c + lane < ns ? exp2f(m_u - M) : 0.0f;
+        lw += wgt * l_u;
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const float wk = __shfl(wgt, u, 64);
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                O[e] += wk * x[u][e];
+        }
+    }
+    const float L = wave_sum(lw);
+    if constexpr (PER == 2)  // both values in one 4-byte store (rows are 16-byte aligned)
+        *(uint32_t *)out = (uint32_t)(uint16_t)E::from_f(O[0] / L) |
+                           ((uint32_t)(uint16_t)E::from_f(O[1] / L) << 16);
+    else
+        out[0] = (uint16_t)E::from_f(O[0] / L);
+}
+
 }  // namespace
 
 DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t Hkv, int64_t D,
@@ -1060,14 +1167,27 @@ hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEve
                                 : launch_stream_e<Bf16>(p, stream, e0, e1);
 }
 
+// A segment's fan-in is about NS / (A * NHG) + 1 groups when every launched
+// group holds tiles.  Above 12 the wide merge runs (measured on MI355X: A = 1
+// 9.7 -> 6.6 us, A = 8 6.5 -> 4.9 us), below it the narrow one (fan-in 2-9:
+// 5-6 us, where the wide one measured 0.2-0.9 us slower).
+template <class E, int D>
+static void launch_merge_d(const DecodeParams &p, hipStream_t stream)
+{
+    const dim3 grid(p.Hq * p.A), block(64);
+    if ((long long)p.NS > 12ll * p.A * p.NHG)
+        hipLaunchKernelGGL((k_decode_merge_wide<E, D>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((k_decode_merge<E, D>), grid, block, 0, stream, p);
+}
+
 template <class E>
 static void launch_merge_e(const DecodeParams &p, hipStream_t stream)
 {
-    const dim3 grid(p.Hq * p.A), block(64);
     if (p.D == 64)
-        hipLaunchKernelGGL((k_decode_merge<E, 64>), grid, block, 0, stream, p);
+        launch_merge_d<E, 64>(p, stream);
     else
-        hipLaunchKernelGGL((k_decode_merge<E, 128>), grid, block, 0, stream, p);
+        launch_merge_d<E, 128>(p, stream);
 }
 
 hipError_t launch_decode_merge(const DecodeParams &p, hipStream_t stream)
