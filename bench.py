@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "ragged", "long"])
     ap.add_argument("--layers", type=int, default=8, help="layer caches rotated over the steps")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="decode entries A in place of the workload's own (0 = as configured); "
+                         "the workload is then named <workload>_decode_A<batch>")
     ap.add_argument("--waves", type=int, default=0,
                     help="waves sharing the keys (0 = the device's resident waves)")
     ap.add_argument("--kernel", type=int, default=0, help="0 tuned stream, 1 readable")
@@ -105,6 +108,20 @@ def source_digest(family, csrc=CSRC):
         h.update(" ".join(text.split()).encode())
         h.update(b"\0")
     return h.hexdigest()[:16]
+
+
+def decode_label(args):
+    """Name of the decode workload: the configuration, and the batch size when overridden."""
+    return f"{args.workload}_decode" + (f"_A{args.batch}" if args.batch else "")
+
+
+def decode_config(args, dtype):
+    import workloads
+    cfg = workloads.config(args.workload, dtype=dtype)
+    if args.batch:
+        cfg = workloads.config(args.workload, dtype=dtype, A=args.batch,
+                               S=max(cfg["S"], args.batch))
+    return cfg
 
 
 def measured_traffic(kernel, workload):
@@ -183,7 +200,7 @@ def main():
         "vs_baseline": None,
         "dtype": args.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}_decode", "A": A, "slots": S, "capacity": C,
+        "config": {"workload": decode_label(args), "A": A, "slots": S, "capacity": C,
                    "h_q": Hq, "h_kv": Hkv, "head_dim": D, "rope_base": cfg["base"],
                    "ctx_mean": round(float(ctx.mean()), 1), "ctx_max": int(ctx.max()),
                    "layers_rotated": L, "waves": args.waves or "resident",
@@ -203,7 +220,7 @@ def main():
             "unit": "GB/s",
             "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic("k_decode_stream" if args.kernel == 0 else
-                                        "k_decode_readable", f"{args.workload}_decode"
+                                        "k_decode_readable", decode_label(args)
                                         + ("_f16" if args.dtype == "f16" else "")),
             "avg_launch_ms": round(attn_avg, 5),
             "algorithmic_bytes_per_launch": kv_bytes,
@@ -237,7 +254,7 @@ def decode_leg(args, hip, dtype, K, W, L):
     import workloads
 
     dev = torch.device("cuda:0")
-    cfg = workloads.config(args.workload, dtype=dtype)
+    cfg = decode_config(args, dtype)
     A, S, C, Hq, Hkv, D = (cfg[k] for k in ("A", "S", "C", "Hq", "Hkv", "D"))
     print(f"[bench] drawing {args.workload} {dtype} inputs + {L} layer caches", file=sys.stderr,
           flush=True)
@@ -318,7 +335,7 @@ def bench_f16(args, hip):
     ms = d["wall"] * 1e3 / K
     attn = float(np.mean(d["attn_ms"]))
     kv = d["kv_bytes"]
-    res = {"decode": {"workload": f"{args.workload}_decode", "steps": K,
+    res = {"decode": {"workload": decode_label(args), "steps": K,
                       "ms_per_step": round(ms, 4), "value": round(kv / (ms * 1e-3) / 1e9, 1),
                       "unit": "GB/s",
                       "roofline": {"kernel": "k_decode_stream", "bound": "hbm",
