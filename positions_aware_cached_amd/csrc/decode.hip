@@ -570,13 +570,13 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             const uint32_t off = (uint32_t)min(jt + b * 16 + n, jend - 1) * slotb + lg * 16;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kn[b][ks] = *(const u32x4 *)(kb + off + ks * 64);
+                kn[b][ks] = __builtin_nontemporal_load((const u32x4 *)(kb + off + ks * 64));
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const uint32_t off = (uint32_t)min(jt + i * KPI + lane / LPK, jend - 1) * slotb +
                                  (lane % LPK) * 16;
-            vn[i] = *(const u32x4 *)(vb + off);
+            vn[i] = __builtin_nontemporal_load((const u32x4 *)(vb + off));
         }
     };
     auto store_tile = [&]() {
