@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published
+EVENT_STRIDE = 4          # timed decode steps per step whose kernel carries HIP events
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak, published
 METRIC = "decode attn step: KV GB/s and % of HBM peak; tokens/s at A rows, ctx"
 
@@ -280,31 +281,34 @@ def decode_leg(args, hip, dtype, K, W, L):
     io_bytes = A * Hq * D * 2 * 2 + 2 * A * Hkv * D * 2 * 2 + 8 * A
     total_bytes = kv_bytes + io_bytes
 
-    evs = []
-    for _ in range(K):
+    # The attention kernel's own duration: the library stamps start and end
+    # events into the dispatch of every EVENT_STRIDE-th timed step.  A stamped
+    # dispatch costs the step about 5 us more on MI355X (measured: 113.7 vs
+    # 118-120 us per Llama-like step), so the other steps run unstamped.
+    stamped = [i for i in range(K) if i % EVENT_STRIDE == EVENT_STRIDE - 1] or [K - 1]
+    evs = {}
+    for i in stamped:
         pair = (ctypes.c_void_p * 2)()
         for j in range(2):
             h = ctypes.c_void_p()
             assert hip.hipEventCreate(ctypes.byref(h)) == 0
             pair[j] = h.value
-        evs.append(pair)
+        evs[i] = pair
 
     print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
     for i in range(W):
         call(i % L)
     torch.cuda.synchronize()
-    # timed region: K steps; the library stamps the attention kernel's own
-    # start/end into the events through its dispatch (no extra queue commands)
     print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        call(i % L, attn_events=evs[i])
+        call(i % L, attn_events=evs.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert int(status.item()) == 0, "device reported an index error"
     attn_ms = []
-    for pair in evs:
+    for pair in evs.values():
         f = ctypes.c_float()
         assert hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(pair[0]),
                                        ctypes.c_void_p(pair[1])) == 0

@@ -197,10 +197,14 @@ __device__ __forceinline__ float wave_max(float v)
 // lane, in double, rounded once), the G rotated queries as matrix-core B
 // operands, and -- in the wave that holds the segment's last tile -- RoPE of
 // k_new and the store of K' and V at (row, pos), staged in LDS so that the
-// wave attends to exactly the stored bytes.
+// wave attends to exactly the stored bytes.  The queries, key and value come
+// into registers with the segment's first tile and move to LDS at its start.
 //
 // Per 32-key tile: the next tile is in flight in registers (K in operand
-// order, V in row order, 16 B per lane) while this one is computed from LDS:
+// order, V in row order, 16 B per lane, non-temporal loads: every cached byte
+// is read once per step) while this one is computed from LDS; as soon as it
+// has landed the tile after it is issued, so the end of one segment and the
+// start of the next run with loads in flight:
 //   QK  v_mfma_f32_16x16x32_{bf16,f16}: A = 16 keys x 32 dims of K, B = 32 dims
 //       x 16 columns holding the parts of the FP32 rotated query heads; lane l
 //       ends with the scores of keys 4 (l / 16) + i of column l % 16.
@@ -215,6 +219,12 @@ __device__ __forceinline__ float wave_max(float v)
 // (GCLS 16).  BF16: three parts reproduce an FP32 value exactly (GCLS <= 4),
 // two carry it to 2^-16 relative (GCLS 8, 16); FP16: two parts, 2^-22.
 constexpr int kTile = 32;
+#ifdef MLLM_STAMPS
+__device__ unsigned long long mllm_stamps[4096 * 8];
+#define STAMP(k, v) do { if (threadIdx.x == 0) mllm_stamps[blockIdx.x * 8 + (k)] = (v); } while (0)
+#else
+#define STAMP(k, v) do { } while (0)
+#endif
 
 template <int GCLS, class E>
 struct Cols {
@@ -254,14 +264,6 @@ __device__ __forceinline__ float class_sum(float v)
 // Its result for arguments below -126 is flushed to zero, which only drops
 // weights under 2^-126 of the running maximum.
 __device__ __forceinline__ float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// One 16-B global -> LDS load per active lane: lane l's bytes land at
-// lds_base + 16 l (the LDS base is wave-uniform).
-__device__ __forceinline__ void lds_dma16(const void *g, void *lds_base)
-{
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
-}
 
 // v shifted up by K lanes within each row of 16 lanes, 0 in the row's first K
 // lanes (DPP row_shr)
@@ -392,33 +394,33 @@ __device__ __forceinline__ int plan_waves(int launched, long long NT)
 
 // First tile of group w.  With two resident groups per compute unit the
 // groups of the first half are each unit's first-dispatched group, whose waves
-// win the instruction-issue ties of their SIMDs and run ahead (measured on
-// MI355X: with equal shares the second half finished 12-13 % later, on every
-// batch shape).  When the segments are long (at least 32 tiles each on
-// average), a group's time follows its tile count, and the first half gets
-// weight kWA, the second kWB: t0(w) = floor(W(w) NT / W(NW)), W the running
-// weight (37 : 27, the best of the ratios 1.29, 1.32, 1.37, 1.43, 1.5 and 1.6
-// measured on the Llama-like and long-context batches).  With short segments
-// the per-segment work dominates and the tile weights measured no faster, so
-// the split stays uniform (weight 1 each), as it does when NW is odd or there
-// are fewer than four tiles per group (no range is empty).
-constexpr long long kWA = 37, kWB = 27;
+// win the instruction-issue ties of their SIMDs and run ahead.  When the
+// segments are long (at least 32 tiles each on average), a group's time
+// follows its tile count, and the first half gets weight plan_wa, the second
+// plan_wb: t0(w) = floor(W(w) NT / W(NW)), W the running weight.  The host
+// picks the ratio by the work per tile (measured on MI355X with the K/V tiles
+// read non-temporally: 46 : 30 with up to 4 query heads per kv head, 41 : 28
+// with 5-16, the best of the ratios 1.37, 1.46, 1.53 and 1.60 on the
+// Llama-like and long-context batches).  With short segments the per-segment
+// work dominates and the tile weights measured no faster, so the split stays
+// uniform (weight 1 each), as it does when NW is odd or there are fewer than
+// four tiles per group (no range is empty).
 __device__ __forceinline__ bool plan_is_weighted(const DecodeParams &p, long long NT, int NW)
 {
     return p.plan_weighted && !(NW & 1) && NT >= 4ll * NW &&
            NT >= 32ll * p.A * p.NHG;
 }
-__device__ __forceinline__ long long plan_weight(int w, bool weighted, int NW)
+__device__ __forceinline__ long long plan_weight(const DecodeParams &p, int w, bool weighted, int NW)
 {
     if (!weighted)
         return w;
     const long long C = NW >> 1;
-    return w <= C ? kWA * w : kWA * C + kWB * (w - C);
+    return w <= C ? (long long)p.plan_wa * w : (long long)p.plan_wa * C + (long long)p.plan_wb * (w - C);
 }
 __device__ __forceinline__ long long plan_t0(const DecodeParams &p, int w, long long NT, int NW)
 {
     const bool wt = plan_is_weighted(p, NT, NW);
-    return plan_weight(w, wt, NW) * NT / plan_weight(NW, wt, NW);
+    return plan_weight(p, w, wt, NW) * NT / plan_weight(p, NW, wt, NW);
 }
 
 // Group that owns global tile t: the largest w with t0(w) <= t, i.e. with
@@ -426,11 +428,12 @@ __device__ __forceinline__ long long plan_t0(const DecodeParams &p, int w, long 
 __device__ __forceinline__ int plan_wave_of(const DecodeParams &p, long long t, long long NT, int NW)
 {
     const bool wt = plan_is_weighted(p, NT, NW);
-    const long long X = ((t + 1) * plan_weight(NW, wt, NW) - 1) / NT;
+    const long long X = ((t + 1) * plan_weight(p, NW, wt, NW) - 1) / NT;
     if (!wt)
         return (int)X;
     const int C = NW >> 1;
-    const long long w = X <= kWA * C ? X / kWA : C + (X - kWA * C) / kWB;
+    const long long wa = p.plan_wa, wb = p.plan_wb;
+    const long long w = X <= wa * C ? X / wa : C + (X - wa * C) / wb;
     return (int)min(w, (long long)NW - 1);
 }
 
@@ -467,6 +470,9 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     constexpr float HEADROOM = 8.0f;       // log2 growth of a column max before O is rescaled
 
     const int w = blockIdx.x;  // work group: one wave per kv head of a head group
+    STAMP(0, wall_clock64());
+    STAMP(4, ((unsigned long long)__builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)) << 32) |
+                 __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11)));
     const int wi = threadIdx.x >> 6, HG = p.HG, NHG = p.NHG;
     const int lane = threadIdx.x & 63, n = lane & 15, lg = lane >> 4;
     const int G = p.G, Hkv = p.Hkv;
@@ -497,6 +503,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
         if (lane == 0)
             p.plan[p.A] = run;
     }
+    STAMP(1, wall_clock64());
     if (w >= NW)
         return;
     const long long t0 = plan_t0(p, w, NT, NW), t1 = plan_t0(p, w + 1, NT, NW);
@@ -541,22 +548,26 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
         j = (int)(loc - (long long)h * na);
     }
 
-    // ---- the tile in flight (nxt); cur is (a, h, j), h the head group (this
-    // wave's kv head is h HG + wi)
-    int nxa = a, nxh = h, nxj = j, nxna = na, nxrow = row, nxpos = pos;
-    long long nxbase = ebase;
-    auto advance = [&]() {  // nxt := the tile after nxt
-        if (++nxj < nxna)
+    // ---- tiles ahead of the current one (a, h, j), h the head group (this
+    // wave's kv head is h HG + wi): nxt has its loads in flight while the
+    // current tile is computed, nx2 is issued once nxt has landed
+    struct TilePos {
+        int a, h, j, na, row, pos;
+        long long base;
+    };
+    TilePos nxt = {a, h, j, na, row, pos, ebase}, nx2 = nxt;
+    auto advance = [&](TilePos &x) {  // x := the tile after x
+        if (++x.j < x.na)
             return;
-        nxj = 0;
-        if (++nxh < NHG)
+        x.j = 0;
+        if (++x.h < NHG)
             return;
-        nxh = 0;
-        nxbase += (long long)NHG * nxna;
+        x.h = 0;
+        x.base += (long long)NHG * x.na;
         do {
-            ++nxa;
-            entry(nxa, nxpos, nxrow, nxna);
-        } while (nxna == 0 && nxa < p.A);
+            ++x.a;
+            entry(x.a, x.pos, x.row, x.na);
+        } while (x.na == 0 && x.a < p.A);
     };
 
     auto seg_base = [&](int srow, int hg, const uint16_t *blk) {
@@ -606,26 +617,32 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
                 u32x4{0u, 0u, 0u, 0u};
     };
 
-    // ---- segment inputs: the G query heads, the new key and the new value go
-    // straight from memory into LDS (16 B per lane per load), issued before
-    // the segment's first tile and read only after that tile has arrived
+    // ---- segment inputs: the G query heads (16 B per lane per load), and for
+    // the group that holds the segment's last tile the new key and value,
+    // loaded into registers with the segment's first tile and moved to LDS
+    // when the segment starts
+    constexpr int QCH = D / 8;                          // 16-B chunks per head
+    constexpr int NQL = (GCLS * QCH + 63) / 64;         // query loads per lane
     bool own_pre = false;
     int cs_entry = -1;  // entry whose cos/sin sit in cs/sn
-    auto fetch_segment = [&](int ea, int hg, long long eb, int ena) {
-        constexpr int QCH = D / 8;  // 16-B chunks per head
+    u32x4 qreg[NQL], kvreg = {0u, 0u, 0u, 0u};  // kvreg: lanes < LPK the key, next LPK the value
+#pragma unroll
+    for (int i = 0; i < NQL; ++i)
+        qreg[i] = u32x4{0u, 0u, 0u, 0u};
+    auto load_segment = [&](int ea, int hg, long long eb, int ena) {
         const int eh = hg * HG + wi;
         const uint16_t *qs = p.q + ea * p.q_sa + eh * G * p.q_sh;
 #pragma unroll
-        for (int c0 = 0; c0 < GCLS * QCH; c0 += 64) {
-            const int c = c0 + lane;
+        for (int i = 0; i < NQL; ++i) {
+            const int c = i * 64 + lane;
             if (c < G * QCH)
-                lds_dma16(qs + (c / QCH) * p.q_sh + (c % QCH) * 8, qlds + c0 * 8);
+                qreg[i] = *(const u32x4 *)(qs + (c / QCH) * p.q_sh + (c % QCH) * 8);
         }
         own_pre = eb + (long long)hg * ena + ena - 1 < t1;  // holds the last tile
-        if (own_pre && lane < LPK) {
-            lds_dma16(p.k_new + ea * p.kn_sa + eh * p.kn_sh + lane * 8, kraw);
-            lds_dma16(p.v_new + ea * p.vn_sa + eh * p.vn_sh + lane * 8, newv);
-        }
+        if (own_pre && lane < 2 * LPK)
+            kvreg = lane < LPK
+                        ? *(const u32x4 *)(p.k_new + ea * p.kn_sa + eh * p.kn_sh + lane * 8)
+                        : *(const u32x4 *)(p.v_new + ea * p.vn_sa + eh * p.vn_sh + (lane - LPK) * 8);
     };
     // cos/sin of entry ea's angles, written by wave 0 for the whole group (ALU
     // only; the heads of an entry share them)
@@ -651,7 +668,15 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
         pos = epos;
         nkeys = epos + 1;
         owner = own_pre;
-        __syncthreads();  // cs/sn and the segment inputs written by other lanes
+#pragma unroll
+        for (int i = 0; i < NQL; ++i) {
+            const int c = i * 64 + lane;
+            if (c < G * QCH)
+                *(u32x4 *)(qlds + c * 8) = qreg[i];
+        }
+        if (owner && lane < 2 * LPK)
+            *(u32x4 *)(lane < LPK ? kraw + lane * 8 : newv + (lane - LPK) * 8) = kvreg;
+        __syncthreads();  // cs/sn from wave 0, the segment inputs from other lanes
         if (owner) {
             const size_t at = ((size_t)erow * p.C + epos) * slot + (size_t)eh * D;
             if (lane < D / 2) {
@@ -664,44 +689,39 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
                 newk[lane] = klo;
                 newk[lane + D / 2] = khi;
             }
-            if (lane < LPK)
-                *(u32x4 *)(p.vc + at + lane * 8) = *(const u32x4 *)(newv + lane * 8);
+            if (lane >= LPK && lane < 2 * LPK)
+                *(u32x4 *)(p.vc + at + (lane - LPK) * 8) = kvreg;
         }
-        // B operands of QK: the parts of the rotated query, by column
-        float qv[KS][8];
+        // B operands of QK: the parts of the rotated query, by column; one
+        // rotation pair of 32-dim blocks (ks, ks + KS/2) at a time
         const unsigned char *qrow = (const unsigned char *)qlds + (ccol ? chead : 0) * D * 2;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 v = *(const u32x4 *)(qrow + (ks * 32 + lg * 8) * 2);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                qv[ks][2 * e] = E::lo(v[e]);
-                qv[ks][2 * e + 1] = E::hi(v[e]);
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS / 2; ++ks)
+        for (int ks = 0; ks < KS / 2; ++ks) {
+            const u32x4 vx = *(const u32x4 *)(qrow + (ks * 32 + lg * 8) * 2);
+            const u32x4 vy = *(const u32x4 *)(qrow + ((ks + KS / 2) * 32 + lg * 8) * 2);
+            float lo[8], hi[8];
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 const int i = ks * 32 + lg * 8 + jj;
-                float lo, hi;
-                rope_pair(qv[ks][jj], qv[ks + KS / 2][jj], cs[i], sn[i], lo, hi);
-                qv[ks][jj] = lo;
-                qv[ks + KS / 2][jj] = hi;
+                const float x = (jj & 1) ? E::hi(vx[jj >> 1]) : E::lo(vx[jj >> 1]);
+                const float y = (jj & 1) ? E::hi(vy[jj >> 1]) : E::lo(vy[jj >> 1]);
+                rope_pair(x, y, cs[i], sn[i], lo[jj], hi[jj]);
             }
 #pragma unroll
-        for (int c = 0; c < NGRP; ++c) {
-            const int part = NGRP == 1 ? min(cpart, NPART - 1) : c;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4 v;
+            for (int c = 0; c < NGRP; ++c) {
+                const int part = NGRP == 1 ? min(cpart, NPART - 1) : c;
+                u32x4 wl, wh;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t b0 = ccol ? E::template part<NPART>(qv[ks][2 * e], part) : 0u;
-                    const uint32_t b1 = ccol ? E::template part<NPART>(qv[ks][2 * e + 1], part) : 0u;
-                    v[e] = b0 | (b1 << 16);
+                    wl[e] = ccol ? E::template part<NPART>(lo[2 * e], part) |
+                                       (E::template part<NPART>(lo[2 * e + 1], part) << 16)
+                                 : 0u;
+                    wh[e] = ccol ? E::template part<NPART>(hi[2 * e], part) |
+                                       (E::template part<NPART>(hi[2 * e + 1], part) << 16)
+                                 : 0u;
                 }
-                bq[c][ks] = __builtin_bit_cast(vec8, v);
+                bq[c][ks] = __builtin_bit_cast(vec8, wl);
+                bq[c][ks + KS / 2] = __builtin_bit_cast(vec8, wh);
             }
         }
         m_run = -INFINITY;
@@ -741,34 +761,37 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
         }
     };
 
-    // ---- first tile
-    fetch_segment(a, h, ebase, na);
+    // ---- first tile, then the next one in flight before the segment's start work
+    load_segment(a, h, ebase, na);
     load_tile(seg_base(row, h, p.kc), seg_base(row, h, p.vc), j * TK, pos + 1);
     angles(a, pos);
     store_tile();
+    if (t0 + 1 < t1) {
+        advance(nxt);
+        load_tile(seg_base(nxt.row, nxt.h, p.kc), seg_base(nxt.row, nxt.h, p.vc), nxt.j * TK,
+                  nxt.pos + 1);
+    }
     start_segment(h, row, pos);
     if (owner && j == na - 1)
         patch_tile(pos - j * TK);
+    if (t0 + 1 < t1 && nxt.j == 0)
+        load_segment(nxt.a, nxt.h, nxt.base, nxt.na);
     __syncthreads();
+    STAMP(2, wall_clock64());
+    STAMP(5, (unsigned long long)(t1 - t0));
 
+    // Per tile t: tile t is in LDS, t + 1 (nxt) in flight.  After t is
+    // computed, t + 1 moves to LDS and t + 2 (nx2) is issued at once, so the
+    // segment end / start work that follows runs with loads in flight.
     for (long long t = t0; t < t1; ++t) {
-        const bool more = t + 1 < t1;
-        if (more) {
-            advance();
-            // a segment starts at tile 0 except the wave's first one
-            if (nxj == 0)
-                fetch_segment(nxa, nxh, nxbase, nxna);
-            load_tile(seg_base(nxrow, nxh, p.kc), seg_base(nxrow, nxh, p.vc), nxj * TK,
-                      nxpos + 1);
-            // cos/sin of a segment that starts at the next tile, while the
-            // loads are in flight (the last reads of cs/sn were fenced by the
-            // barrier that ended the previous iteration)
-            if (nxj == 0)
-                angles(nxa, nxpos);
-        }
-        const bool seg_ends = !more || nxj == 0;
+        const bool more = t + 1 < t1, more2 = t + 2 < t1;
+        // cos/sin of a segment that starts at t + 1, used at the end of this
+        // iteration (the last reads of cs/sn were fenced by the barrier that
+        // ended the previous iteration; the barrier below publishes these)
+        if (more && nxt.j == 0)
+            angles(nxt.a, nxt.pos);
+        const bool seg_ends = !more || nxt.j == 0;
         const int jt = j * TK;
-
         // QK: lane (n, lg) gets keys jt + 16 b + 4 lg + i of column n
         f32x4 acc[NB][NGRP];
 #pragma unroll
@@ -863,27 +886,39 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
         }
         __syncthreads();  // LDS of tile t fully read
 
-        // the one wait per tile: tile t+1 (and the segment inputs issued
-        // before it) into LDS; then this segment's partial and the next
-        // segment's start, whose stores drain during the next tile
-        if (more)
+        // the one wait per tile: t + 1 into LDS; then t + 2 goes out before
+        // this segment's partial and the next segment's start
+        if (more) {
             store_tile();
+            if (more2) {
+                nx2 = nxt;
+                advance(nx2);
+                load_tile(seg_base(nx2.row, nx2.h, p.kc), seg_base(nx2.row, nx2.h, p.vc),
+                          nx2.j * TK, nx2.pos + 1);
+            }
+        }
         if (seg_ends)
             end_segment(a, h);
         if (more) {
             if (seg_ends)
-                start_segment(nxh, nxrow, nxpos);
-            a = nxa;
-            h = nxh;
-            j = nxj;
-            na = nxna;
-            row = nxrow;
-            ebase = nxbase;
+                start_segment(nxt.h, nxt.row, nxt.pos);
+            a = nxt.a;
+            h = nxt.h;
+            j = nxt.j;
+            na = nxt.na;
+            row = nxt.row;
+            ebase = nxt.base;
+            nxt = nx2;
             if (owner && j == na - 1)
                 patch_tile(pos - j * TK);
+            // the segment inputs of t + 2, once this segment's start has read the registers
+            if (more2 && nxt.j == 0)
+                load_segment(nxt.a, nxt.h, nxt.base, nxt.na);
             __syncthreads();
         }
     }
+
+    STAMP(3, wall_clock64());
 }
 
 // ---------------------------------------------------------------- R4
@@ -1264,4 +1299,10 @@ hipError_t launch_decode_readable(const DecodeParams &p, hipStream_t stream, hip
     return hipGetLastError();
 }
 
+#ifdef MLLM_STAMPS
+extern "C" int mllm_debug_stamps(void *dst, size_t bytes)
+{
+    return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(mllm_stamps), bytes);
+}
+#endif
 }  // namespace mllm

@@ -599,6 +599,10 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     // the device's resident groups, two per compute unit: the plan gives the
     // first-dispatched half a larger share (see the decode kernel's plan)
     p.plan_weighted = waves == 0 && p.NS == 2 * device_cus(d.device) ? 1 : 0;
+    // more query heads per kv head, more work per tile: a smaller lead of the
+    // first-dispatched groups (ratios measured on MI355X)
+    p.plan_wa = G <= 4 ? 46 : 41;
+    p.plan_wb = G <= 4 ? 30 : 28;
     p.dtype = d.dtype;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     fill_inv_freq(p.inv_freq, rope->base, D);
