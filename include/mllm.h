@@ -224,6 +224,32 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
                                         uint64_t workspace_bytes, int32_t *status_dev,
                                         const mllm_decode_opts *opts, void *stream);
 
+/*
+ * The decode step of mllm_decode_rope_store_attn without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * partial results and the plan live in a scratch array of the library
+ * (64 MiB per device, held from the first call on a device until the process
+ * ends); the call allocates nothing.  Arguments, results, checks and errors are
+ * those of mllm_decode_rope_store_attn, with the same output bits for the same
+ * inputs and options.  A call that needs more scratch than 64 MiB (about
+ * A * H_q * D * 4 + (A * H_kv + waves of the launch) * G * (D + 2) * 4 bytes)
+ * returns MLLM_ERR_UNSUPPORTED before any launch.  Every call on one device
+ * shares that device's scratch: calls that overlap in time on one device race
+ * (run them on one stream, or one at a time).
+ */
+mllm_status mllm_decode_rope_store_attn_noalloc(mllm_cache *cache, int32_t layer,
+                                                const mllm_tensor_view *q,
+                                                const mllm_tensor_view *k_new,
+                                                const mllm_tensor_view *v_new,
+                                                const int32_t *positions_dev,
+                                                const int32_t *cache_rows_dev, int32_t A,
+                                                const int32_t *host_mirror,
+                                                const mllm_rope_desc *rope,
+                                                const mllm_tensor_view *out,
+                                                int32_t *status_dev,
+                                                const mllm_decode_opts *opts, void *stream);
+
 /* Workspace bytes needed by mllm_prefill_rope_store_attn and
  * mllm_prefill_chunk_rope_store_attn for A entries of (up to) T tokens and
  * h_q query heads: a cos/sin table of A * T * head_dim / 2 float pairs. */

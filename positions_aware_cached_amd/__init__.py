@@ -29,7 +29,8 @@ EXPORTS = ("mllm_abi_version", "mllm_last_error", "mllm_cache_bytes", "mllm_cach
            "mllm_prefill_rope_store_attn", "mllm_prefill_chunk_rope_store_attn",
            "mllm_cache_set_row_length", "mllm_sched_create", "mllm_sched_free",
            "mllm_sched_max_sequence_length", "mllm_sched_submit", "mllm_sched_stop",
-           "mllm_sched_cancel", "mllm_sched_boundary", "mllm_sched_counts")
+           "mllm_sched_cancel", "mllm_sched_boundary", "mllm_sched_counts",
+           "mllm_decode_rope_store_attn_noalloc")
 
 
 class MllmError(RuntimeError):
@@ -113,6 +114,9 @@ def load(path=LIB_PATH):
     L.mllm_decode_rope_store_attn.argtypes = [
         vp, i32, P(TensorView), P(TensorView), P(TensorView), vp, vp, i32, P(i32),
         P(RopeDesc), P(TensorView), vp, u64, vp, P(DecodeOpts), vp]
+    L.mllm_decode_rope_store_attn_noalloc.argtypes = [
+        vp, i32, P(TensorView), P(TensorView), P(TensorView), vp, vp, i32, P(i32),
+        P(RopeDesc), P(TensorView), vp, P(DecodeOpts), vp]
     L.mllm_prefill_workspace_size.argtypes = [vp, i32, i32, i32, P(u64)]
     L.mllm_prefill_rope_store_attn.argtypes = [
         vp, i32, P(TensorView), P(TensorView), P(TensorView), vp, P(i32), i32, i32,
@@ -350,6 +354,24 @@ def decode_rope_store_attn(cache, layer, q, k_new, v_new, positions, rows, out, 
         ctypes.byref(view(v_new)), _ptr(positions), _ptr(rows), A, hm, ctypes.byref(rope),
         ctypes.byref(view(out)), ws_ptr, ws_bytes, _ptr(status), ctypes.byref(o),
         _stream(stream)))
+
+
+def decode_rope_store_attn_noalloc(cache, layer, q, k_new, v_new, positions, rows, out, base,
+                                   host_mirror=None, status=None, waves=0, kernel=0,
+                                   attn_events=None, stream=None):
+    """The decode step without a workspace (mllm_decode_rope_store_attn_noalloc):
+    the library's per-device scratch holds the partials; arguments as for
+    decode_rope_store_attn."""
+    A = q.shape[0]
+    rope = RopeDesc(float(base), q.shape[-1], 0)
+    o = _opts(waves, kernel, attn_events)
+    hm = None
+    if host_mirror is not None:
+        hm_t, hm = _host_i32(host_mirror, 2 * A, "host_mirror")
+    _check(load().mllm_decode_rope_store_attn_noalloc(
+        cache.handle, layer, ctypes.byref(view(q)), ctypes.byref(view(k_new)),
+        ctypes.byref(view(v_new)), _ptr(positions), _ptr(rows), A, hm, ctypes.byref(rope),
+        ctypes.byref(view(out)), _ptr(status), ctypes.byref(o), _stream(stream)))
 
 
 def prefill_workspace_size(cache, A, T, h_q):

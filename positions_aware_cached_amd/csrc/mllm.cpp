@@ -6,6 +6,7 @@
 // (microLLM-rocm ARCHITECTURE.md, "Tensor N0 invariants": negative dims and
 // strides are rejected, zero-size dims are legal, a view must lie inside its
 // storage, unsupported operations fail explicitly).
+#include <hip/hip_runtime.h>
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -465,17 +466,47 @@ mllm_status mllm_decode_workspace_size(const mllm_cache *cache, int32_t A, int32
     return ok();
 }
 
-mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
-                                        const mllm_tensor_view *q,
-                                        const mllm_tensor_view *k_new,
-                                        const mllm_tensor_view *v_new,
-                                        const int32_t *positions_dev,
-                                        const int32_t *cache_rows_dev, int32_t A,
-                                        const int32_t *host_mirror,
-                                        const mllm_rope_desc *rope,
-                                        const mllm_tensor_view *out, void *workspace,
-                                        uint64_t workspace_bytes, int32_t *status_dev,
-                                        const mllm_decode_opts *opts, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free decode entry point: partial results and the
+// plan prefix of a decode call, in place of a caller's workspace.  One copy
+// per device, at an address read once per device with hipGetSymbolAddress
+// (the array's name in host code is only a stand-in, never a device address);
+// every call on a device shares it.
+constexpr uint64_t kDecodeScratchBytes = 64ull << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+// Device address of `scratch` on the current device (which must be `device`).
+mllm_status scratch_address(int device, void **ptr)
+{
+    static std::mutex mu;
+    static std::map<int, void *> addr;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = addr.find(device);
+    if (it == addr.end()) {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress(decode scratch)");
+        if (!p || ((uintptr_t)p) % 256 != 0)
+            return fail(MLLM_ERR_DEVICE, "decode scratch has no 256-byte aligned address");
+        it = addr.emplace(device, p).first;
+    }
+    *ptr = it->second;
+    return MLLM_OK;
+}
+
+// One decode step (mllm_decode_rope_store_attn), its partials in `workspace`
+// or, with use_scratch, in this device's `scratch`.
+mllm_status decode_impl(mllm_cache *cache, int32_t layer, const mllm_tensor_view *q,
+                        const mllm_tensor_view *k_new, const mllm_tensor_view *v_new,
+                        const int32_t *positions_dev, const int32_t *cache_rows_dev, int32_t A,
+                        const int32_t *host_mirror, const mllm_rope_desc *rope,
+                        const mllm_tensor_view *out, void *workspace, uint64_t workspace_bytes,
+                        bool use_scratch, int32_t *status_dev, const mllm_decode_opts *opts,
+                        void *stream)
 {
     if (!cache)
         return fail(MLLM_ERR_INVALID_ARG, "cache is null");
@@ -534,8 +565,18 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
         }
     }
     const int nw_bound = waves > 0 ? waves : MLLM_MAX_WAVES;
-    const mllm::DecodeWorkspace wl = mllm::decode_workspace_layout(A, Hq, d.h_kv, D, nw_bound);
-    if (A > 0) {
+    mllm::DecodeWorkspace wl = mllm::decode_workspace_layout(A, Hq, d.h_kv, D, nw_bound);
+    if (use_scratch) {
+        // the bytes with no partial slot beyond one per (entry, kv head): a
+        // lower bound, so a call this rejects needs no device query
+        const uint64_t least = mllm::decode_workspace_layout(A, Hq, d.h_kv, D, 0).total;
+        if (least > kDecodeScratchBytes)
+            return fail(MLLM_ERR_UNSUPPORTED,
+                        "A = %d, H_q = %lld needs at least %llu scratch bytes; the "
+                        "allocation-free call holds %llu", A, (long long)Hq,
+                        (unsigned long long)least, (unsigned long long)kDecodeScratchBytes);
+        wl.total = 0;  // library memory: no caller range to check against the others
+    } else if (A > 0) {
         if (!workspace)
             return fail(MLLM_ERR_WORKSPACE, "workspace is null");
         if (((uintptr_t)workspace) % 256 != 0)
@@ -581,10 +622,12 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     p.out = (uint16_t *)out->data;
     p.o_sa = out->stride[0];
     p.o_sh = out->stride[1];
-    p.qrot = (float *)((char *)workspace + wl.qrot_off);
-    p.part_o = (float *)((char *)workspace + wl.part_o_off);
-    p.part_ml = (float *)((char *)workspace + wl.part_ml_off);
-    p.plan = (long long *)((char *)workspace + wl.plan_off);
+    if (!use_scratch) {
+        p.qrot = (float *)((char *)workspace + wl.qrot_off);
+        p.part_o = (float *)((char *)workspace + wl.part_o_off);
+        p.part_ml = (float *)((char *)workspace + wl.part_ml_off);
+        p.plan = (long long *)((char *)workspace + wl.plan_off);
+    }
     p.status = status_dev;
     p.A = A;
     p.S = d.slots;
@@ -598,6 +641,21 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
     p.NS = launch_groups(waves, d.device, D, G, p.HG, d.dtype);
     // the device's resident groups, two per compute unit: the plan gives the
     // first-dispatched half a larger share (see the decode kernel's plan)
+    if (use_scratch) {
+        // the exact size for the groups this launch runs (NS groups of HG waves)
+        wl = mllm::decode_workspace_layout(A, Hq, d.h_kv, D, (int64_t)p.NS * p.HG);
+        if (wl.total > kDecodeScratchBytes)
+            return fail(MLLM_ERR_UNSUPPORTED,
+                        "this decode call needs %llu scratch bytes; the allocation-free call "
+                        "holds %llu", (unsigned long long)wl.total,
+                        (unsigned long long)kDecodeScratchBytes);
+        if ((st = scratch_address(d.device, &workspace)))
+            return st;
+        p.qrot = (float *)((char *)workspace + wl.qrot_off);
+        p.part_o = (float *)((char *)workspace + wl.part_o_off);
+        p.part_ml = (float *)((char *)workspace + wl.part_ml_off);
+        p.plan = (long long *)((char *)workspace + wl.plan_off);
+    }
     p.plan_weighted = waves == 0 && p.NS == 2 * device_cus(d.device) ? 1 : 0;
     // more query heads per kv head, more work per tile: a smaller lead of the
     // first-dispatched groups (ratios measured on MI355X)
@@ -631,6 +689,43 @@ mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
         }
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mllm_status mllm_decode_rope_store_attn(mllm_cache *cache, int32_t layer,
+                                        const mllm_tensor_view *q,
+                                        const mllm_tensor_view *k_new,
+                                        const mllm_tensor_view *v_new,
+                                        const int32_t *positions_dev,
+                                        const int32_t *cache_rows_dev, int32_t A,
+                                        const int32_t *host_mirror,
+                                        const mllm_rope_desc *rope,
+                                        const mllm_tensor_view *out, void *workspace,
+                                        uint64_t workspace_bytes, int32_t *status_dev,
+                                        const mllm_decode_opts *opts, void *stream)
+{
+    return decode_impl(cache, layer, q, k_new, v_new, positions_dev, cache_rows_dev, A,
+                       host_mirror, rope, out, workspace, workspace_bytes, false, status_dev,
+                       opts, stream);
+}
+
+mllm_status mllm_decode_rope_store_attn_noalloc(mllm_cache *cache, int32_t layer,
+                                                const mllm_tensor_view *q,
+                                                const mllm_tensor_view *k_new,
+                                                const mllm_tensor_view *v_new,
+                                                const int32_t *positions_dev,
+                                                const int32_t *cache_rows_dev, int32_t A,
+                                                const int32_t *host_mirror,
+                                                const mllm_rope_desc *rope,
+                                                const mllm_tensor_view *out,
+                                                int32_t *status_dev,
+                                                const mllm_decode_opts *opts, void *stream)
+{
+    return decode_impl(cache, layer, q, k_new, v_new, positions_dev, cache_rows_dev, A,
+                       host_mirror, rope, out, nullptr, 0, true, status_dev, opts, stream);
 }
 
 mllm_status mllm_prefill_workspace_size(const mllm_cache *cache, int32_t A, int32_t T,

@@ -342,3 +342,44 @@ def test_host_arrays_checked_by_the_binding():
         pac._host_i32([1, 2, 3], 4, "host_mirror")
     with pytest.raises(ValueError, match="host memory"):
         pac._host_i32(torch.empty(4, dtype=torch.int32, device="meta"), 4, "rows_host")
+
+
+def call_decode_noalloc(fc, A=4, Hq=4, q=None, k=None, v=None, out=None, pos=FAKE + 0x10000,
+                        rows=FAKE + 0x20000, layer=0, opts=None):
+    D = fc.D
+    q = q or fake_view([A, Hq, D], FAKE + 0x1000000)
+    k = k or fake_view([A, fc.Hkv, D], FAKE + 0x2000000)
+    v = v or fake_view([A, fc.Hkv, D], FAKE + 0x3000000)
+    out = out or fake_view([A, Hq, D], FAKE + 0x4000000)
+    rope = pac.RopeDesc(1e4, D, 0)
+    o = opts or pac.DecodeOpts()
+    return pac.load().mllm_decode_rope_store_attn_noalloc(
+        fc.cache.handle, layer, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+        ctypes.c_void_p(pos), ctypes.c_void_p(rows), A, None, ctypes.byref(rope),
+        ctypes.byref(out), None, ctypes.byref(o), None)
+
+
+def test_decode_noalloc_checks_and_limit():
+    """The allocation-free decode call makes the checks of the workspace call,
+    and refuses a call whose partials need more than its 64 MiB scratch before
+    any device query."""
+    fc = FakeCache()
+    expect(call_decode_noalloc(fc, layer=2), "INVALID_ARG")
+    expect(call_decode_noalloc(fc, pos=0), "INVALID_ARG")
+    expect(call_decode_noalloc(fc, out=fake_view([4, 4, fc.D], fc.k[0] + 4096)), "ALIAS")
+    o = pac.DecodeOpts()
+    o.kernel = 5
+    expect(call_decode_noalloc(fc, opts=o), "INVALID_ARG")
+    assert call_decode_noalloc(fc, A=0) == 0, pac.last_error()
+    # 20000 entries x 64 query heads x 64 dims: the FP32 rotated queries alone
+    # take 328 MB of scratch
+    big = FakeCache(Hkv=8, S=20000, C=16)
+    A, Hq, D = 20000, 64, big.D
+    G = 1 << 30
+    st = call_decode_noalloc(big, A=A, Hq=Hq, q=fake_view([A, Hq, D], FAKE + 1 * G),
+                             k=fake_view([A, 8, D], FAKE + 2 * G),
+                             v=fake_view([A, 8, D], FAKE + 3 * G),
+                             out=fake_view([A, Hq, D], FAKE + 4 * G),
+                             pos=FAKE + 5 * G, rows=FAKE + 6 * G)
+    expect(st, "UNSUPPORTED")
+    assert "scratch" in pac.last_error()
