@@ -118,10 +118,14 @@ typedef struct {
 
 typedef struct mllm_cache mllm_cache; /* opaque */
 
-/* ABI version of the loaded library (MLLM_ABI_VERSION). */
+/* ABI version of the loaded library (MLLM_ABI_VERSION): the C ABI is versioned
+ * ("Stable integration boundary": the seam is a C-compatible descriptor with
+ * explicit stream and workspace, and the C ABI carries a version). */
 int mllm_abi_version(void);
 
-/* Thread-local text of the last failure on this thread ("" after success). */
+/* Thread-local text of the last failure on this thread ("" after success):
+ * every rejected call fails explicitly with a status and this message ("Tensor
+ * N0 invariants": unsupported operations fail explicitly). */
 const char *mllm_last_error(void);
 
 /* Exact device bytes of a cache: num_layers * 2 * slots * capacity * h_kv *
@@ -129,24 +133,31 @@ const char *mllm_last_error(void);
  * layer/head/element-size allocation formula). */
 mllm_status mllm_cache_bytes(const mllm_cache_desc *desc, uint64_t *bytes);
 
-/* Allocate an engine-owned cache with hipMalloc on desc->device.  Contents are
- * not initialized; every row starts logically empty (length 0). */
+/* Allocate an engine-owned cache with hipMalloc on desc->device ("Tensor
+ * ownership boundary": a shared cache allocation that persists while rows come
+ * and go; the same kernels consume engine-owned or caller-owned memory).
+ * Contents are not initialized; every row starts logically empty (length 0). */
 mllm_status mllm_cache_alloc(const mllm_cache_desc *desc, mllm_cache **out);
 
-/* Wrap caller-owned device memory (e.g. torch tensors) as a cache.  k_layers
+/* Wrap caller-owned device memory (e.g. torch tensors) as a cache ("Tensor
+ * ownership boundary": ownership is never inferred from a pointer, so the same
+ * kernels run on engine-owned or PyTorch-owned allocations).  k_layers
  * and v_layers hold num_layers pointers, each to a dense [slots, capacity,
  * h_kv, head_dim] block of desc->dtype, 16-byte aligned.  The caller keeps ownership and
  * must keep the memory alive until mllm_cache_free. */
 mllm_status mllm_cache_wrap(const mllm_cache_desc *desc, void *const *k_layers,
                             void *const *v_layers, mllm_cache **out);
 
-/* Release the cache object (and its memory if engine-owned).  NULL is a no-op. */
+/* Release the cache object, and its memory if engine-owned ("Tensor ownership
+ * boundary": storage owns an allocation, views do not).  NULL is a no-op. */
 mllm_status mllm_cache_free(mllm_cache *cache);
 
-/* Device pointers of one layer's K and V blocks. */
+/* Device pointers of one layer's K and V blocks: non-owning, valid while the
+ * cache lives ("Tensor ownership boundary": views are non-owning). */
 mllm_status mllm_cache_layer(const mllm_cache *cache, int32_t layer, void **k, void **v);
 
-/* Copy of the descriptor the cache was created with. */
+/* Copy of the descriptor the cache was created with ("Stable integration
+ * boundary": the cache crosses the ABI as a C descriptor). */
 mllm_status mllm_cache_get_desc(const mllm_cache *cache, mllm_cache_desc *desc);
 
 /* Logical reset of one row ("Tensor ownership boundary": the shared allocation
@@ -155,17 +166,22 @@ mllm_status mllm_cache_get_desc(const mllm_cache *cache, mllm_cache_desc *desc);
  * memory. */
 mllm_status mllm_cache_reset_row(mllm_cache *cache, int32_t row);
 
-/* Host-side logical length of one row: T after a prefill, max(len, pos + 1)
- * after a decode made with a host mirror, 0 after a reset. */
+/* Host-side logical length of one row ("Tensor ownership boundary": a row's
+ * active prefix grows with its decode steps and falls to zero on reset): T after
+ * a prefill, max(len, pos + 1) after a decode made with a host mirror, 0 after a
+ * reset. */
 mllm_status mllm_cache_row_length(const mllm_cache *cache, int32_t row, int32_t *len);
 
 /* Declare a row's logical length, 0 <= len <= capacity (MLLM_ERR_OUT_OF_RANGE
  * otherwise): for a caller that filled or restored the row by other means, or
- * decoded without a host mirror.  Touches no device memory. */
+ * decoded without a host mirror ("Tensor ownership boundary": the scheduler
+ * above the model primitives owns each row's state).  Touches no device
+ * memory. */
 mllm_status mllm_cache_set_row_length(mllm_cache *cache, int32_t row, int32_t len);
 
 /* Workspace bytes needed by mllm_decode_rope_store_attn for A entries and h_q
- * query heads with the given opts (may be NULL).  max_position bounds every
+ * query heads with the given opts (may be NULL) ("Stable integration
+ * boundary": the workspace is explicit and caller-owned).  max_position bounds every
  * position of the call (-1 = capacity - 1); the current layout's size does not
  * depend on it.  The size is the same for every position, so one workspace serves
  * every step of a decode loop. */
@@ -252,7 +268,8 @@ mllm_status mllm_decode_rope_store_attn_noalloc(mllm_cache *cache, int32_t layer
 
 /* Workspace bytes needed by mllm_prefill_rope_store_attn and
  * mllm_prefill_chunk_rope_store_attn for A entries of (up to) T tokens and
- * h_q query heads: a cos/sin table of A * T * head_dim / 2 float pairs. */
+ * h_q query heads: a cos/sin table of A * T * head_dim / 2 float pairs
+ * ("Stable integration boundary": the workspace is explicit and caller-owned). */
 mllm_status mllm_prefill_workspace_size(const mllm_cache *cache, int32_t A, int32_t T,
                                         int32_t h_q, uint64_t *bytes);
 
@@ -364,28 +381,38 @@ typedef struct {
                       next token is stored at (the row's length); retired: mllm_end */
 } mllm_sched_entry;
 
-/* A scheduler over every row of `cache`; each row must be empty (length 0,
+/* A scheduler over every row of `cache` ("Tensor ownership boundary": the
+ * scheduler owns the request-to-row map); each row must be empty (length 0,
  * else MLLM_ERR_ROW_BUSY).  max_sequence_length: 0 = the cache capacity,
- * else 1..capacity (MLLM_ERR_OUT_OF_RANGE). */
+ * else 1..capacity (MLLM_ERR_OUT_OF_RANGE; the same section bounds the
+ * persistent cache by it, zero keeping the model maximum). */
 mllm_status mllm_sched_create(mllm_cache *cache, int32_t max_sequence_length, mllm_sched **out);
+/* Release the scheduler (not the cache: "Tensor ownership boundary", the shared
+ * cache allocation persists). */
 mllm_status mllm_sched_free(mllm_sched *sched);
-/* The bound in force (the cache capacity when created with 0). */
+/* The bound in force, the cache capacity when created with 0 ("Tensor ownership
+ * boundary": max_sequence_length bounds the persistent cache). */
 mllm_status mllm_sched_max_sequence_length(const mllm_sched *sched, int32_t *len);
 
-/* Queue a request, first in first out.  prompt_len >= 1, max_new_tokens >= 0
+/* Queue a request, first in first out; it is admitted at a later step boundary
+ * ("Tensor ownership boundary": admission only at scheduler-step boundaries).
+ * prompt_len >= 1, max_new_tokens >= 0
  * (MLLM_ERR_INVALID_ARG); prompt_len + max_new_tokens <= max_sequence_length
  * (MLLM_ERR_OUT_OF_RANGE); ids unique among queued and active requests
  * (MLLM_ERR_INVALID_ARG). */
 mllm_status mllm_sched_submit(mllm_sched *sched, int64_t request_id, int32_t prompt_len,
                               int32_t max_new_tokens);
-/* End a request: stop (the caller saw its stop token) takes effect at the next
+/* End a request ("Tensor ownership boundary": a row is reset on length, stop or
+ * cancel): stop (the caller saw its stop token) takes effect at the next
  * boundary; cancel removes a queued request at once and ends an active one at
  * the next boundary.  Unknown id: MLLM_ERR_INVALID_ARG. */
 mllm_status mllm_sched_stop(mllm_sched *sched, int64_t request_id);
 mllm_status mllm_sched_cancel(mllm_sched *sched, int64_t request_id);
 
 /*
- * Step boundary.  In order:
+ * Step boundary ("Tensor ownership boundary": admission only at step
+ * boundaries, reset on length/stop/cancel, the lowest free slot reused).  In
+ * order:
  *  1. retire: each active request that was cancelled (MLLM_END_CANCEL) or
  *     stopped (MLLM_END_STOP), or whose row holds prompt_len + max_new_tokens
  *     positions (MLLM_END_LENGTH; each decode step stores one token), leaves
@@ -406,7 +433,8 @@ mllm_status mllm_sched_boundary(mllm_sched *sched, mllm_sched_entry *admitted,
                                 mllm_sched_entry *decode, int32_t decode_cap, int32_t *n_decode,
                                 mllm_sched_entry *retired, int32_t retired_cap,
                                 int32_t *n_retired);
-/* Requests waiting in the queue and requests holding a row. */
+/* Requests waiting in the queue and requests holding a row ("Tensor ownership
+ * boundary": the scheduler exposes snapshots of its state). */
 mllm_status mllm_sched_counts(const mllm_sched *sched, int32_t *queued, int32_t *active);
 
 #ifdef __cplusplus

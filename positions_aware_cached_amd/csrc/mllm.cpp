@@ -269,6 +269,13 @@ int device_cus(int device)
     return cus;
 }
 
+// A one-dimensional launch of `blocks` work groups of `threads` work-items:
+// the dispatch packet counts the grid's work-items in 32 bits.
+bool grid_fits(int64_t blocks, int threads)
+{
+    return blocks >= 0 && blocks < (int64_t(1) << 32) / threads;
+}
+
 mllm_status check_device_current(int device)
 {
     int cur = -1;
@@ -526,9 +533,12 @@ mllm_status decode_impl(mllm_cache *cache, int32_t layer, const mllm_tensor_view
         return fail(MLLM_ERR_INVALID_ARG, "H_q %lld must be a positive multiple of H_kv %d",
                     (long long)Hq, d.h_kv);
     const int G = (int)(Hq / d.h_kv);
-    if ((int64_t)A * Hq >= (1ll << 31))
-        return fail(MLLM_ERR_UNSUPPORTED, "A * H_q = %lld must stay below 2^31 (one wave each)",
-                    (long long)A * Hq);
+    // the merge and readable launches run one 64-lane wave per (entry, query
+    // head), the readable store one 256-lane block per entry
+    if (!grid_fits((int64_t)A * Hq, 64) || !grid_fits(A, 256))
+        return fail(MLLM_ERR_UNSUPPORTED,
+                    "A * H_q = %lld must stay below 2^26 (one 64-lane wave each in a "
+                    "one-dimensional grid) and A below 2^24", (long long)A * Hq);
     if (G > 16)
         return fail(MLLM_ERR_UNSUPPORTED, "group size H_q/H_kv = %d exceeds 16", G);
     mllm_status st = check_rope(rope, D);
@@ -779,15 +789,22 @@ mllm_status prefill_call(mllm_cache *cache, int32_t layer, const mllm_tensor_vie
         return fail(MLLM_ERR_INVALID_ARG, "H_q %lld must be a positive multiple of H_kv %d",
                     (long long)Hq, d.h_kv);
     const int G = (int)(Hq / d.h_kv);
-    if ((int64_t)A * T * Hq >= (1ll << 31))
-        return fail(MLLM_ERR_UNSUPPORTED, "A * T * H_q = %lld must stay below 2^31",
-                    (long long)A * T * Hq);
     mllm_status st = check_rope(rope, D);
     if (st)
         return st;
     int waves_unused, kernel;
     if ((st = resolve_opts(opts, &waves_unused, &kernel)))
         return st;
+    // one-dimensional grids: the store kernel one 64-lane wave per (entry,
+    // token), the matrix-core kernel one 256-lane block per (entry, query head,
+    // 128 queries), the readable kernel one 64-lane wave per (entry, token,
+    // query head)
+    if (!grid_fits((int64_t)A * T, 64) ||
+        (kernel == 1 ? !grid_fits((int64_t)A * T * Hq, 64)
+                     : !grid_fits((int64_t)A * Hq * ((T + 127) / 128), 256)))
+        return fail(MLLM_ERR_UNSUPPORTED,
+                    "A = %d, T = %d, H_q = %lld exceed a one-dimensional launch grid "
+                    "(2^32 work-items)", A, T, (long long)Hq);
     Range rq, rk, rv, ro;
     const int64_t sq[4] = {A, T, Hq, D}, skv[4] = {A, T, d.h_kv, D};
     if ((st = check_view(q, "q", 4, sq, d.device, d.dtype, false, &rq)) ||

@@ -233,7 +233,7 @@ def test_wrap_rejections():
 
 
 def call_prefill(fc, A=2, T=16, Hq=4, rows_host=(0, 1), ws=FAKE + 0x40000000, ws_bytes=1 << 30,
-                 q=None, out=None):
+                 q=None, out=None, opts=None):
     D = fc.D
     q = q or fake_view([A, T, Hq, D], FAKE + 0x1000000)
     k = fake_view([A, T, fc.Hkv, D], FAKE + 0x2000000)
@@ -244,7 +244,7 @@ def call_prefill(fc, A=2, T=16, Hq=4, rows_host=(0, 1), ws=FAKE + 0x40000000, ws
     return pac.load().mllm_prefill_rope_store_attn(
         fc.cache.handle, 0, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
         ctypes.c_void_p(FAKE + 0x20000), rh, A, T, ctypes.byref(rope), ctypes.byref(out),
-        ctypes.c_void_p(ws), ws_bytes, None, None)
+        ctypes.c_void_p(ws), ws_bytes, ctypes.byref(opts) if opts is not None else None, None)
 
 
 def test_prefill_rejections_before_device():
@@ -325,11 +325,31 @@ def test_dtype_rules():
 
 
 def test_grid_size_limits():
-    """Flattened launch grids: A * H_q (decode) and A * T * H_q (prefill) must
-    stay below 2^31."""
+    """One-dimensional launch grids count their work-items in 32 bits: the host
+    refuses a call whose grid would not fit, before any launch (the decode
+    merge: one 64-lane wave per entry and query head, so A * H_q < 2^26; the
+    readable prefill: A * T * H_q < 2^26; the matrix-core prefill: A * H_q *
+    ceil(T / 128) 256-lane blocks < 2^24)."""
     fc = FakeCache(S=8, C=256)
+    G = 1 << 30
+    views = lambda A, Hq: dict(q=fake_view([A, Hq, fc.D], FAKE + 1 * G),
+                               k=fake_view([A, fc.Hkv, fc.D], FAKE + 2 * G),
+                               v=fake_view([A, fc.Hkv, fc.D], FAKE + 3 * G),
+                               out=fake_view([A, Hq, fc.D], FAKE + 4 * G),
+                               pos=FAKE + 5 * G, rows=FAKE + 6 * G, mirror=None)
+    A = 1 << 24
+    expect(call_decode(fc, A=A, Hq=4, **views(A, 4)), "UNSUPPORTED")          # 2^26 waves
+    st = call_decode(fc, A=A - 1, Hq=4, **views(A - 1, 4))                     # just below
+    assert pac.STATUS[st] != "UNSUPPORTED", pac.last_error()
+    # readable prefill: 2 x 256 tokens x 2^17 heads = 2^26 waves; the matrix-core
+    # kernel takes the same shape (2^19 blocks)
+    Hq = 1 << 17
+    ro = pac.DecodeOpts()
+    ro.kernel = 1
+    expect(call_prefill(fc, A=2, T=256, Hq=Hq, rows_host=(0, 1), opts=ro), "UNSUPPORTED")
+    st = call_prefill(fc, A=2, T=256, Hq=Hq, rows_host=(0, 1))
+    assert "grid" not in pac.last_error(), pac.last_error()
     big = 1 << 29
-    expect(call_decode(fc, A=big, Hq=4, mirror=None), "UNSUPPORTED")
     expect(call_prefill(fc, A=2, T=256, Hq=big // 64 * 32, rows_host=(0, 1)), "UNSUPPORTED")
 
 
@@ -383,3 +403,31 @@ def test_decode_noalloc_checks_and_limit():
                              pos=FAKE + 5 * G, rows=FAKE + 6 * G)
     expect(st, "UNSUPPORTED")
     assert "scratch" in pac.last_error()
+
+
+# Section titles of the pages that define the boundary's operations.
+SECTIONS = ("Tensor ownership boundary", "Attention layout boundary", "Tensor N0 invariants",
+            "Stable integration boundary", "Correctness-first workflow", "Public interfaces",
+            "Acceptance rule")
+
+
+def test_every_declaration_cites_its_section():
+    """Each mllm_* declaration of include/mllm.h is preceded by a comment that
+    names the page section defining it (the allocation-free call names instead
+    the callers it is for)."""
+    text = open(HEADER).read()
+    token = re.compile(r"/\*.*?\*/|\b(?:mllm_status|int|const char \*)\s*(mllm_[a-z_]+)\s*\(",
+                       re.S)
+    last, seen = "", []
+    for m in token.finditer(text):
+        if m.group(0).startswith("/*"):
+            last = " ".join(re.sub(r"^\s*\*", " ", l) for l in m.group(0).splitlines())
+            last = " ".join(last.split())
+            continue
+        name = m.group(1)
+        seen.append(name)
+        ok = any(t in last for t in SECTIONS)
+        if name.endswith("_noalloc"):
+            ok = "cannot allocate" in last
+        assert ok, f"{name}: no section cited in its comment: {last[:120]}"
+    assert set(seen) == set(declared_functions())
