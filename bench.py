@@ -60,6 +60,13 @@ def parse():
                     help="also time the slot manager's step boundary (0 = skip)")
     ap.add_argument("--f16-steps", type=int, default=50,
                     help="also time the decode step and the prefill with FP16 storage (0 = skip)")
+    ap.add_argument("--other-decode-steps", type=int, default=-1,
+                    help="timed steps of the ragged and long-context decode legs (-1 = --steps, "
+                         "0 = skip)")
+    ap.add_argument("--other-layers", type=int, default=4,
+                    help="layer caches rotated in the ragged and long-context legs")
+    ap.add_argument("--ceiling-reps", type=int, default=5,
+                    help="timed reads per launch shape of the streaming-read ceiling (0 = skip)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times): the reference that "
                          "scales the HBM byte counters of a profiler run")
@@ -242,6 +249,21 @@ def main():
         call(0)  # a fresh layer-0 step: the oracle sample is compared with it
         torch.cuda.synchronize()
         res["cpu_baseline"] = cpu_baseline(args, cfg, inp, d["layers"], pos_h, rows_h, out)
+    # the ragged and long-context decode batches, after the headline leg's memory is freed
+    K2 = args.steps if args.other_decode_steps < 0 else args.other_decode_steps
+    if K2 > 0 and args.workload == "llama3_8b" and not args.batch:
+        del d, inp, cache, out, ws, call
+        torch.cuda.empty_cache()
+        for w in ("ragged", "long"):
+            res[w] = bench_decode_workload(args, hip, w, K2)
+            torch.cuda.empty_cache()
+    if args.ceiling_reps > 0:
+        ceil = read_ceiling(args.ceiling_reps)
+        res["ceiling"] = ceil
+        for leg in [res] + [res[w] for w in ("ragged", "long") if w in res]:
+            leg["roofline"]["ceiling_gbs"] = ceil["ceiling_gbs"]
+            leg["roofline"]["frac_of_ceiling"] = round(
+                leg["roofline"]["achieved"] / ceil["ceiling_gbs"], 4)
     print(json.dumps(res), flush=True)
 
 
@@ -329,6 +351,80 @@ def decode_leg(args, hip, dtype, K, W, L):
     return dict(cfg=cfg, inp=inp, cache=cache, pos=pos, rows=rows, out=out, ws=ws, mirror=mirror,
                 call=call, status=status, layers=layers, pos_h=pos_h, rows_h=rows_h, ctx=ctx, kv_bytes=kv_bytes,
                 total_bytes=total_bytes, wall=wall, attn_ms=attn_ms, step_ms=step_ms)
+
+
+def bench_decode_workload(args, hip, workload, K):
+    """The decode step on another batch shape ("ragged": 200 rows of 256 with
+    log-uniform positions; "long": 8 rows of 32K context, 64 query heads): K
+    timed steps after the headline's warm-up count, rotating over
+    --other-layers layer caches; figures as in the headline line."""
+    import argparse
+    a = argparse.Namespace(**vars(args))
+    a.workload, a.batch = workload, 0
+    L = max(1, args.other_layers)
+    d = decode_leg(a, hip, "bf16", K, args.warmup, L)
+    cfg, ctx, kv = d["cfg"], d["ctx"], d["kv_bytes"]
+    ms = d["wall"] * 1e3 / K
+    attn = float(np.mean(d["attn_ms"]))
+    gbs = kv / (ms * 1e-3) / 1e9
+    agbs = kv / (attn * 1e-3) / 1e9
+    label = decode_label(a)
+    res = {"workload": label, "A": cfg["A"], "slots": cfg["S"], "capacity": cfg["C"],
+           "h_q": cfg["Hq"], "h_kv": cfg["Hkv"], "head_dim": cfg["D"],
+           "ctx_mean": round(float(ctx.mean()), 1), "ctx_max": int(ctx.max()),
+           "layers_rotated": L, "steps": K, "ms_per_step": round(ms, 4),
+           "value": round(gbs, 1), "unit": "GB/s",
+           "pct_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+           "tokens_per_s": round(cfg["A"] / (ms * 1e-3), 1),
+           "step_ms_median": round(percentile(d["step_ms"], 50), 4),
+           "kv_bytes_per_step": kv,
+           "roofline": {"kernel": "k_decode_stream", "bound": "hbm", "achieved": round(agbs, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(agbs / PEAK_HBM_GBS, 4),
+                        "traffic": measured_traffic("k_decode_stream", label),
+                        "avg_launch_ms": round(attn, 5), "algorithmic_bytes_per_launch": kv}}
+    del d
+    return res
+
+
+def read_ceiling(reps):
+    """Streaming-read ceiling of the device: a plain non-temporal read of 4 GiB
+    (positions_aware_cached_amd/probe/read_ceiling.hip), timed over `reps`
+    reads per launch shape; the best median over three shapes (blocks of 256
+    lanes per compute unit x loads in flight per lane)."""
+    import torch
+    path = os.path.join(ROOT, "positions_aware_cached_amd", "libreadprobe.so")
+    L = ctypes.CDLL(path)
+    L.mllm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    n = 4 << 30
+    buf = torch.ones(n, dtype=torch.uint8, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 4 * 256, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = None
+    for bpc, unroll in ((3, 2), (2, 4), (1, 8)):
+        ms = []
+        for r in range(reps + 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = L.mllm_probe_read(buf.data_ptr(), n, cus * bpc, unroll, sink.data_ptr(), stream)
+            e1.record()
+            assert rc == 0, f"read probe launch failed ({rc})"
+            torch.cuda.synchronize()
+            if r:
+                ms.append(e0.elapsed_time(e1))
+        med = float(np.median(ms))
+        gbs = n / (med * 1e-3) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, bpc, unroll, med)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"ceiling_gbs": round(best[0], 1), "frac_of_peak": round(best[0] / PEAK_HBM_GBS, 4),
+            "bytes": n, "ms": round(best[3], 4),
+            "launch": f"{best[1]} blocks of 256 lanes per CU, {best[2]} 16-B loads in flight per "
+                      "lane, non-temporal", "reads_per_shape": reps}
 
 
 def bench_f16(args, hip):
@@ -524,11 +620,37 @@ def bench_prefill(args, hip, name, K, dtype="bf16"):
             "hbm_gbs_step": round(hbm / wall / 1e9, 1)}
 
 
+def cpu_model():
+    """Model name of the host CPU (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def oracle_threads():
+    """Worker threads for the all-core oracle runs: the host's CPUs, at most 16
+    (the CPU share of one GPU on the measurement hosts)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def cpu_baseline(args, cfg, inp, layers, pos_h, rows_h, out_gpu):
-    """The CPU oracle (single thread, as it stands) on a bounded sample of the
-    same workload: entries one by one, each on a host copy of its row's prefix,
-    layer after layer of the rotated caches, until the time budget is spent.
-    The layer-0 outputs are also compared with the GPU's layer-0 outputs."""
+    """The CPU oracle, as it stands, on bounded samples of the same workload.
+
+    Single thread: entries one by one, each on a host copy of its row's prefix,
+    layer after layer of the rotated caches, until --cpu-seconds of oracle time.
+    All cores: the same entries again, `oracle_threads()` at a time from a
+    thread pool (the oracle's C entry point runs without the GIL); only the
+    oracle calls are timed.  The layer-0 outputs are compared with the GPU's
+    layer-0 outputs.  Then the prefill oracle on a stated sample of the
+    16 x 1024 prefill, on one thread and on the pool."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     import workloads
 
@@ -539,20 +661,30 @@ def cpu_baseline(args, cfg, inp, layers, pos_h, rows_h, out_gpu):
         widen = lambda b: np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
     else:
         widen = oracle.bf16_to_f32
-    done, kv, elapsed, worst = 0, 0, 0.0, 0.0
+    done, kv, elapsed, worst = [], 0, 0.0, 0.0
     t_start = time.perf_counter()
     out_bits = workloads.bits(out_gpu)
-    for layer, (Kc, Vc) in enumerate(layers):
+
+    def prefix(layer, a):
+        Kc, Vc = layers[layer]
+        p, r = int(pos_h[a]), int(rows_h[a])
+        Km = workloads.bits(Kc[r, :p + 1]).reshape(1, p + 1, Hkv, D).copy()
+        Vm = workloads.bits(Vc[r, :p + 1]).reshape(1, p + 1, Hkv, D).copy()
+        return Km, Vm
+
+    def run(a, Km, Vm):
+        p = int(pos_h[a])
+        return orc.decode_step(qb[a:a + 1], kb[a:a + 1], vb[a:a + 1], [p], [0], Km, Vm,
+                               cfg["base"], dtype=cfg["dtype"])
+
+    for layer in range(len(layers)):
         for a in range(len(pos_h)):
-            p, r = int(pos_h[a]), int(rows_h[a])
-            Km = workloads.bits(Kc[r, :p + 1]).reshape(1, p + 1, Hkv, D).copy()
-            Vm = workloads.bits(Vc[r, :p + 1]).reshape(1, p + 1, Hkv, D).copy()
+            Km, Vm = prefix(layer, a)
             t0 = time.perf_counter()
-            o = orc.decode_step(qb[a:a + 1], kb[a:a + 1], vb[a:a + 1], [p], [0], Km, Vm,
-                                cfg["base"], dtype=cfg["dtype"])
+            o = run(a, Km, Vm)
             elapsed += time.perf_counter() - t0
-            done += 1
-            kv += (p + 1) * Hkv * D * 2 * 2
+            done.append((layer, a))
+            kv += (int(pos_h[a]) + 1) * Hkv * D * 2 * 2
             if layer == 0:
                 worst = max(worst, float(np.abs(widen(o[0]).astype(np.float64) -
                                                 widen(out_bits[a]).astype(np.float64)).max()))
@@ -561,12 +693,71 @@ def cpu_baseline(args, cfg, inp, layers, pos_h, rows_h, out_gpu):
         else:
             continue
         break
-    return {"value": round(kv / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} entry-steps of the {args.workload} decode step ({len(pos_h)} "
-                      f"entries per layer, layers 0..{done // len(pos_h)} of the rotated "
-                      f"caches), {kv} KV bytes, {elapsed:.2f} s single-threaded",
-            "tokens_per_s": round(done / elapsed, 3),
-            "gpu_vs_oracle_max_abs": worst}
+
+    nthr = oracle_threads()
+    par = 0.0
+    with ThreadPoolExecutor(max_workers=nthr) as pool:
+        for c0 in range(0, len(done), nthr):
+            batch = [(a,) + prefix(layer, a) for layer, a in done[c0:c0 + nthr]]
+            t0 = time.perf_counter()
+            list(pool.map(lambda x: run(*x), batch))
+            par += time.perf_counter() - t0
+    n = len(done)
+    pf = prefill_oracle_sample(nthr)
+    return {"value": round(kv / par / 1e9, 4), "unit": "GB/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{n} entry-steps of the {args.workload} decode step ({len(pos_h)} entries "
+                      f"per layer, layers 0..{(n - 1) // len(pos_h)} of the rotated caches), {kv} "
+                      f"KV bytes; {nthr} threads each calling the unchanged single-threaded "
+                      f"oracle on one entry, {par:.2f} s of oracle calls",
+            "tokens_per_s": round(n / par, 3),
+            "single_thread": {"value": round(kv / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "seconds": round(elapsed, 2),
+                              "tokens_per_s": round(n / elapsed, 3)},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "gpu_vs_oracle_max_abs": worst,
+            "prefill": pf}
+
+
+def prefill_oracle_sample(nthr):
+    """The prefill oracle on the 16 x 1024 prefill configuration, sampled: every
+    8th query (t = 7, 15, ..., 1023; each over its t + 1 keys, all 32 query
+    heads, after storing all 1024 tokens), row 0 on one thread, then all 16
+    rows on the thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    import workloads
+
+    cfg = workloads.config("prefill")
+    A, T, Hq, D = cfg["A"], cfg["T"], cfg["Hq"], cfg["D"]
+    inp = workloads.draw_prefill(cfg, device="cuda")
+    qb, kb, vb = (workloads.bits(inp[k]) for k in ("q", "k_new", "v_new"))
+    Kc, Vc = workloads.bits(inp["Kc"]).copy(), workloads.bits(inp["Vc"]).copy()
+    rows = np.asarray(inp["rows"], dtype=np.int32)
+    del inp
+    t_list = np.arange(7, T, 8, dtype=np.int32)
+    orc = oracle.default()
+    flops_row = 4.0 * D * Hq * float(np.sum(t_list.astype(np.float64) + 1.0))
+
+    def row(a):
+        orc.prefill(qb[a:a + 1], kb[a:a + 1], vb[a:a + 1], rows[a:a + 1], Kc, Vc, cfg["base"],
+                    t_list=t_list)
+
+    t0 = time.perf_counter()
+    row(0)
+    one = time.perf_counter() - t0
+    with ThreadPoolExecutor(max_workers=nthr) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(row, range(A)))
+        allr = time.perf_counter() - t0
+    return {"workload": f"prefill_{A}x{T}", "unit": "GFLOP/s",
+            "sample": f"queries t = 7, 15, ..., {T - 1} of each row (every 8th, each over its "
+                      f"t + 1 keys, {Hq} query heads), after the store of all {T} tokens; "
+                      f"{flops_row / 1e9:.2f} GFLOP of attention per row",
+            "single_thread": {"rows": 1, "seconds": round(one, 2),
+                              "value": round(flops_row / one / 1e9, 3)},
+            "all_cores": {"rows": A, "threads": nthr, "seconds": round(allr, 2),
+                          "value": round(A * flops_row / allr / 1e9, 3)}}
 
 
 if __name__ == "__main__":

@@ -26,12 +26,21 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.cpp")) + glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+PROBE_SRC = os.path.join(HERE, "probe", "read_ceiling.hip")
+PROBE_LIB = os.path.join(HERE, "libreadprobe.so")
+
+
 def build(out=LIB, verbose=False, jobs=8):
-    """Compile every source (in parallel) and link out; returns out."""
+    """Compile every source (in parallel) and link out; also the read-ceiling
+    probe library that bench.py loads (measurement code, a library of its
+    own).  Returns out."""
     srcs = sources()
     tmpdir = tempfile.mkdtemp(prefix="mllm_build_")
     try:
-        return _build_in(srcs, tmpdir, out, verbose, jobs)
+        res = _build_in(srcs, tmpdir, out, verbose, jobs)
+        if out == LIB:
+            _build_in([PROBE_SRC], tmpdir, PROBE_LIB, verbose, jobs)
+        return res
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
 
