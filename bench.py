@@ -7,7 +7,9 @@ over every row's prefix with the keys of all rows shared evenly by the resident
 waves, then the cross-wave merge to the BF16 output.
 Steps rotate over several layer caches (as a multi-layer decode does), so a
 step never finds its K/V bytes left in the 256 MB last-level cache by the
-previous step.
+previous step: 4 layers of 1 GiB by default.  The warm-up reads every rotated
+layer once: the first decode read of a freshly allocated layer measured about
+25 us slower on MI355X than every later one.
 
 Prints one JSON line: KV GB/s (algorithmic K+V prefix bytes per step / step
 time), % of the 8 TB/s HBM peak, tokens/s, the dominant kernel's roofline
@@ -39,7 +41,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "ragged", "long"])
-    ap.add_argument("--layers", type=int, default=8, help="layer caches rotated over the steps")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="layer caches rotated over the steps (at most the warm-up count, so "
+                         "every layer is read once before the timed region)")
     ap.add_argument("--batch", type=int, default=0,
                     help="decode entries A in place of the workload's own (0 = as configured); "
                          "the workload is then named <workload>_decode_A<batch>")

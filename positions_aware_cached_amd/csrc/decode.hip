@@ -287,9 +287,35 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane)
     return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
+// Keeps a wave-uniform value in scalar registers from here on: the compiler
+// would otherwise reload a kernel argument before each use, every reload a
+// scalar memory round trip the wave waits for.
+template <class T>
+__device__ __forceinline__ void pin(T &v)
+{
+    asm volatile("" : "+s"(v));
+}
+
+// The kernel arguments the plan reads, loaded once and pinned.
+struct Entries {
+    const int32_t *positions, *rows;
+    int A, S, C, NHG;
+};
+__device__ __forceinline__ Entries entries_of(const DecodeParams &p)
+{
+    Entries e = {p.positions, p.rows, p.A, p.S, p.C, p.NHG};
+    pin(e.positions);
+    pin(e.rows);
+    pin(e.A);
+    pin(e.S);
+    pin(e.C);
+    pin(e.NHG);
+    return e;
+}
+
 // Tile count of entry x from its position and row: 0 when x >= A or the entry
 // is invalid.  Branch-free, so every lane consumes its loads at this point.
-__device__ __forceinline__ int tiles_of(const DecodeParams &p, int x, int pos, int row)
+__device__ __forceinline__ int tiles_of(const Entries &p, int x, int pos, int row)
 {
     const bool ok = (x < p.A) & (pos >= 0) & (pos < p.C) & (row >= 0) & (row < p.S);
     return ok ? (pos + kTile) / kTile : 0;
@@ -301,7 +327,7 @@ __device__ __forceinline__ int tiles_of(const DecodeParams &p, int x, int pos, i
 struct EntryBlock {
     int pos[4], row[4], na[4];
 };
-__device__ __forceinline__ void load_block(const DecodeParams &p, int c0, int lane, EntryBlock &b)
+__device__ __forceinline__ void load_block(const Entries &p, int c0, int lane, EntryBlock &b)
 {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -320,7 +346,7 @@ struct ScanBlock {
     EntryBlock b;
     int incl[4];
 };
-__device__ __forceinline__ void scan_block(const DecodeParams &p, int c0, int lane, ScanBlock &s)
+__device__ __forceinline__ void scan_block(const Entries &p, int c0, int lane, ScanBlock &s)
 {
     load_block(p, c0, lane, s.b);
 #pragma unroll
@@ -330,7 +356,7 @@ __device__ __forceinline__ void scan_block(const DecodeParams &p, int c0, int la
 
 // NT = NHG * sum_a n(a), on every lane; the first block (entries 0..255) is
 // left in first, so that the plan's later passes need not read it again.
-__device__ long long plan_total(const DecodeParams &p, int lane, ScanBlock &first)
+__device__ long long plan_total(const Entries &p, int lane, ScanBlock &first)
 {
     scan_block(p, 0, lane, first);
     long long s = 0;
@@ -349,7 +375,7 @@ __device__ long long plan_total(const DecodeParams &p, int lane, ScanBlock &firs
 
 // The entry holding global tile t < NT, NHG * E(entry), and the 64-entry chunk
 // around it (lane l: entry ec + l), on every lane.
-__device__ void plan_locate(const DecodeParams &p, long long t, int lane, const ScanBlock &first,
+__device__ void plan_locate(const Entries &p, long long t, int lane, const ScanBlock &first,
                             int &a_out, long long &base_out, int &ec, int &e_pos, int &e_row,
                             int &e_na)
 {
@@ -405,36 +431,50 @@ __device__ __forceinline__ int plan_waves(int launched, long long NT)
 // work dominates and the tile weights measured no faster, so the split stays
 // uniform (weight 1 each), as it does when NW is odd or there are fewer than
 // four tiles per group (no range is empty).
-__device__ __forceinline__ bool plan_is_weighted(const DecodeParams &p, long long NT, int NW)
+// The plan of a launch: NT tiles over NW groups, group w from tile t0(w) =
+// floor(W(w) NT / W(NW)) on, W the running weight (see above); computed once
+// and pinned in scalar registers.
+struct Plan {
+    long long NT, WNW, wa, wb;
+    int NW, half;
+    int weighted;
+};
+__device__ __forceinline__ Plan make_plan(const DecodeParams &p, long long NT, int NW)
 {
-    return p.plan_weighted && !(NW & 1) && NT >= 4ll * NW &&
-           NT >= 32ll * p.A * p.NHG;
+    Plan P;
+    P.NT = NT;
+    P.NW = NW;
+    P.half = NW >> 1;
+    P.weighted = p.plan_weighted && !(NW & 1) && NT >= 4ll * NW &&
+                 NT >= 32ll * p.A * p.NHG;
+    P.wa = P.weighted ? p.plan_wa : 1;
+    P.wb = P.weighted ? p.plan_wb : 1;
+    P.WNW = P.wa * P.half + P.wb * (NW - P.half);
+    pin(P.NT);
+    pin(P.WNW);
+    pin(P.wa);
+    pin(P.wb);
+    pin(P.NW);
+    pin(P.half);
+    return P;
 }
-__device__ __forceinline__ long long plan_weight(const DecodeParams &p, int w, bool weighted, int NW)
+__device__ __forceinline__ long long plan_weight(const Plan &P, int w)
 {
-    if (!weighted)
-        return w;
-    const long long C = NW >> 1;
-    return w <= C ? (long long)p.plan_wa * w : (long long)p.plan_wa * C + (long long)p.plan_wb * (w - C);
+    return w <= P.half ? P.wa * w : P.wa * P.half + P.wb * (w - P.half);
 }
-__device__ __forceinline__ long long plan_t0(const DecodeParams &p, int w, long long NT, int NW)
+__device__ __forceinline__ long long plan_t0(const Plan &P, int w)
 {
-    const bool wt = plan_is_weighted(p, NT, NW);
-    return plan_weight(p, w, wt, NW) * NT / plan_weight(p, NW, wt, NW);
+    return plan_weight(P, w) * P.NT / P.WNW;
 }
 
 // Group that owns global tile t: the largest w with t0(w) <= t, i.e. with
 // W(w) <= X = floor(((t + 1) W(NW) - 1) / NT).
-__device__ __forceinline__ int plan_wave_of(const DecodeParams &p, long long t, long long NT, int NW)
+__device__ __forceinline__ int plan_wave_of(const Plan &P, long long t)
 {
-    const bool wt = plan_is_weighted(p, NT, NW);
-    const long long X = ((t + 1) * plan_weight(p, NW, wt, NW) - 1) / NT;
-    if (!wt)
-        return (int)X;
-    const int C = NW >> 1;
-    const long long wa = p.plan_wa, wb = p.plan_wb;
-    const long long w = X <= wa * C ? X / wa : C + (X - wa * C) / wb;
-    return (int)min(w, (long long)NW - 1);
+    const long long X = ((t + 1) * P.WNW - 1) / P.NT;
+    const long long C = P.half;
+    const long long w = X <= P.wa * C ? X / P.wa : C + (X - P.wa * C) / P.wb;
+    return (int)min(w, (long long)P.NW - 1);
 }
 
 // LDS of one wave: K tile, padded V tile, new key / value (rotated and raw),
@@ -480,8 +520,26 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     const float my_freq = p.inv_freq[lane & (D / 2 - 1)];
 
     // the plan uses min(launched groups, NT) groups, so each owns at least one tile
+    const Entries ent = entries_of(p);
+    // the tensors the segment and tile loads address, pinned like the plan's
+    // arguments (each is needed before the first tile can be requested)
+    const uint16_t *qp = p.q, *knp = p.k_new, *vnp = p.v_new;
+    uint16_t *kcp = p.kc, *vcp = p.vc;
+    long long q_sa = p.q_sa, q_sh = p.q_sh, kn_sa = p.kn_sa, kn_sh = p.kn_sh, vn_sa = p.vn_sa,
+              vn_sh = p.vn_sh;
+    pin(qp);
+    pin(knp);
+    pin(vnp);
+    pin(kcp);
+    pin(vcp);
+    pin(q_sa);
+    pin(q_sh);
+    pin(kn_sa);
+    pin(kn_sh);
+    pin(vn_sa);
+    pin(vn_sh);
     ScanBlock first;
-    const long long NT = plan_total(p, lane, first);
+    const long long NT = plan_total(ent, lane, first);
     const int NW = plan_waves(p.NS, NT);
     if (w == 0 && wi == 0) {
         // the plan's prefix for the merge kernel: tiles before each entry, then NT
@@ -491,7 +549,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             if (c0 == 0)
                 sb = first;
             else
-                scan_block(p, c0, lane, sb);
+                scan_block(ent, c0, lane, sb);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int x = c0 + 64 * k + lane;
@@ -506,7 +564,8 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     STAMP(1, wall_clock64());
     if (w >= NW)
         return;
-    const long long t0 = plan_t0(p, w, NT, NW), t1 = plan_t0(p, w + 1, NT, NW);
+    const Plan P = make_plan(p, NT, NW);
+    const long long t0 = plan_t0(P, w), t1 = plan_t0(P, w + 1);
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     using L = WaveLds<D, GCLS>;
@@ -528,14 +587,14 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     int ec, e_pos, e_row, e_na;
     int a, h, j, na, row, pos;
     long long ebase;
-    plan_locate(p, t0, lane, first, a, ebase, ec, e_pos, e_row, e_na);
+    plan_locate(ent, t0, lane, first, a, ebase, ec, e_pos, e_row, e_na);
     auto entry = [&](int e, int &pos_o, int &row_o, int &na_o) {
         if (e < ec || e >= ec + 64) {  // wave-uniform; once per 64 entries
             ec = e & ~63;
-            const int x = ec + lane, xc = min(x, p.A - 1);
-            e_pos = p.positions[xc];
-            e_row = p.rows[xc];
-            e_na = tiles_of(p, x, e_pos, e_row);
+            const int x = ec + lane, xc = min(x, ent.A - 1);
+            e_pos = ent.positions[xc];
+            e_row = ent.rows[xc];
+            e_na = tiles_of(ent, x, e_pos, e_row);
         }
         pos_o = __shfl(e_pos, e - ec, 64);
         row_o = __shfl(e_row, e - ec, 64);
@@ -567,7 +626,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
         do {
             ++x.a;
             entry(x.a, x.pos, x.row, x.na);
-        } while (x.na == 0 && x.a < p.A);
+        } while (x.na == 0 && x.a < ent.A);
     };
 
     auto seg_base = [&](int srow, int hg, const uint16_t *blk) {
@@ -631,18 +690,18 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
         qreg[i] = u32x4{0u, 0u, 0u, 0u};
     auto load_segment = [&](int ea, int hg, long long eb, int ena) {
         const int eh = hg * HG + wi;
-        const uint16_t *qs = p.q + ea * p.q_sa + eh * G * p.q_sh;
+        const uint16_t *qs = qp + ea * q_sa + eh * G * q_sh;
 #pragma unroll
         for (int i = 0; i < NQL; ++i) {
             const int c = i * 64 + lane;
             if (c < G * QCH)
-                qreg[i] = *(const u32x4 *)(qs + (c / QCH) * p.q_sh + (c % QCH) * 8);
+                qreg[i] = *(const u32x4 *)(qs + (c / QCH) * q_sh + (c % QCH) * 8);
         }
         own_pre = eb + (long long)hg * ena + ena - 1 < t1;  // holds the last tile
         if (own_pre && lane < 2 * LPK)
             kvreg = lane < LPK
-                        ? *(const u32x4 *)(p.k_new + ea * p.kn_sa + eh * p.kn_sh + lane * 8)
-                        : *(const u32x4 *)(p.v_new + ea * p.vn_sa + eh * p.vn_sh + (lane - LPK) * 8);
+                        ? *(const u32x4 *)(knp + ea * kn_sa + eh * kn_sh + lane * 8)
+                        : *(const u32x4 *)(vnp + ea * vn_sa + eh * vn_sh + (lane - LPK) * 8);
     };
     // cos/sin of entry ea's angles, written by wave 0 for the whole group (ALU
     // only; the heads of an entry share them)
@@ -684,13 +743,13 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
                 rope_pair(E::to_f(kraw[lane]), E::to_f(kraw[lane + D / 2]), cs[lane], sn[lane], lo,
                           hi);
                 const uint16_t klo = (uint16_t)E::from_f(lo), khi = (uint16_t)E::from_f(hi);
-                p.kc[at + lane] = klo;
-                p.kc[at + lane + D / 2] = khi;
+                kcp[at + lane] = klo;
+                kcp[at + lane + D / 2] = khi;
                 newk[lane] = klo;
                 newk[lane + D / 2] = khi;
             }
             if (lane >= LPK && lane < 2 * LPK)
-                *(u32x4 *)(p.vc + at + (lane - LPK) * 8) = kvreg;
+                *(u32x4 *)(vcp + at + (lane - LPK) * 8) = kvreg;
         }
         // B operands of QK: the parts of the rotated query, by column; one
         // rotation pair of 32-dim blocks (ks, ks + KS/2) at a time
@@ -763,12 +822,14 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
 
     // ---- first tile, then the next one in flight before the segment's start work
     load_segment(a, h, ebase, na);
-    load_tile(seg_base(row, h, p.kc), seg_base(row, h, p.vc), j * TK, pos + 1);
+    load_tile(seg_base(row, h, kcp), seg_base(row, h, vcp), j * TK, pos + 1);
+    STAMP(6, wall_clock64());
     angles(a, pos);
     store_tile();
+    STAMP(7, wall_clock64());
     if (t0 + 1 < t1) {
         advance(nxt);
-        load_tile(seg_base(nxt.row, nxt.h, p.kc), seg_base(nxt.row, nxt.h, p.vc), nxt.j * TK,
+        load_tile(seg_base(nxt.row, nxt.h, kcp), seg_base(nxt.row, nxt.h, vcp), nxt.j * TK,
                   nxt.pos + 1);
     }
     start_segment(h, row, pos);
@@ -893,7 +954,7 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             if (more2) {
                 nx2 = nxt;
                 advance(nx2);
-                load_tile(seg_base(nx2.row, nx2.h, p.kc), seg_base(nx2.row, nx2.h, p.vc),
+                load_tile(seg_base(nx2.row, nx2.h, kcp), seg_base(nx2.row, nx2.h, vcp),
                           nx2.j * TK, nx2.pos + 1);
             }
         }
@@ -954,9 +1015,10 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
     const int G = p.G, h = hq / G, g = hq - h * G, HG = p.HG, NHG = p.NHG;
     const int hg = h / HG, wi = h - hg * HG;  // head group, wave of the group
     const int NW = plan_waves(p.NS, NT);      // NT >= 1: this entry is valid
+    const Plan P = make_plan(p, NT, NW);
     const int na = (pos + kTile) / kTile;
     const long long ts = before + (long long)hg * na;
-    const int wf = plan_wave_of(p, ts, NT, NW), wl = plan_wave_of(p, ts + na - 1, NT, NW);
+    const int wf = plan_wave_of(P, ts), wl = plan_wave_of(P, ts + na - 1);
     const int ns = wl - wf + 1;
     // partial of group wf + x for this head: (max, sum) and D outputs
     auto slot_of = [&](int x) { return ((size_t)(a * NHG + hg + wf + x) * HG + wi) * G + g; };
@@ -1048,9 +1110,10 @@ __global__ __launch_bounds__(64) void k_decode_merge_wide(DecodeParams p)
     const int G = p.G, h = hq / G, g = hq - h * G, HG = p.HG, NHG = p.NHG;
     const int hg = h / HG, wi = h - hg * HG;  // head group, wave of the group
     const int NW = plan_waves(p.NS, NT);      // NT >= 1: this entry is valid
+    const Plan P = make_plan(p, NT, NW);
     const int na = (pos + kTile) / kTile;
     const long long ts = before + (long long)hg * na;
-    const int wf = plan_wave_of(p, ts, NT, NW), wl = plan_wave_of(p, ts + na - 1, NT, NW);
+    const int wf = plan_wave_of(P, ts), wl = plan_wave_of(P, ts + na - 1);
     const int ns = wl - wf + 1;
     // the partial of group wf + x for this head sits in slot slot0 + x * step:
     // (max, sum) pairs step apart, outputs step * D floats apart (at most
