@@ -12,7 +12,8 @@
 //
 //   k_prefill_store     one wave per (token t, entry a): split-half RoPE of
 //                       k_new -> store in the storage type, v_new bit copy; the wave also
-//                       writes the FP32 cos/sin table row of (a, t).
+//                       writes the FP32 cos/sin table row of its position (one
+//                       row per position in an equal-length prefill).
 //   k_prefill_mfma      the tuned attention: one workgroup of four waves per
 //                       (entry, query head, 128-query tile), FlashAttention-
 //                       style online softmax over 64-key tiles on the matrix
@@ -80,10 +81,17 @@ __device__ __forceinline__ Chunk chunk_of(const PrefillParams &p, int a)
     return c;
 }
 
-// workspace: cos/sin table [A][T][D/2] of float2 (cos, sin), row (a, t) for
-// position s_a + t.  One wave per token: cos/sin of its D/2 angles once (into
-// LDS and the table), then each lane rotates 8 pairs of a kv head with 16-byte
-// loads and stores, and V moves in 16-byte chunks.
+// Row of the cos/sin table for token t of entry a: t in an equal-length
+// prefill (all entries start at position 0), a T + t in a chunk.
+__device__ __forceinline__ size_t table_row(const PrefillParams &p, int a, int t)
+{
+    return p.starts == nullptr ? (size_t)t : (size_t)a * p.T + t;
+}
+
+// workspace: cos/sin table of float2 (cos, sin) rows of D/2 pairs, at most
+// [A][T] rows (see table_row).  One wave per token: cos/sin of its D/2 angles
+// once (into LDS and the table), then each lane rotates 8 pairs of a kv head
+// with 16-byte loads and stores, and V moves in 16-byte chunks.
 template <class E>
 __global__ __launch_bounds__(64) void k_prefill_store(PrefillParams p, float2 *table)
 {
@@ -92,16 +100,24 @@ __global__ __launch_bounds__(64) void k_prefill_store(PrefillParams p, float2 *t
     const int lane = threadIdx.x;
     const int D = p.D, H = D / 2;
     const Chunk ch = chunk_of(p, a);
-    if (!ch.ok || t >= ch.n)
+    // equal-length prefill: every entry holds positions 0 .. T-1, so the table
+    // has one row per position, written by entry 0's waves whatever that
+    // entry's own state; a chunk has a row per (entry, token)
+    const bool shared = p.starts == nullptr;
+    const bool store = ch.ok && t < ch.n;
+    if (!store && !(shared && a == 0))
         return;  // past the entry's length, or an invalid entry: write nothing
-    const int pos = ch.s + t;
+    const int pos = shared ? t : ch.s + t;
     __shared__ float cs[kMaxHalfDim], sn[kMaxHalfDim];
     if (lane < H) {
         float theta = __fmul_rn((float)pos, p.inv_freq[lane]);
         cs[lane] = (float)cos((double)theta);
         sn[lane] = (float)sin((double)theta);
-        table[((size_t)a * p.T + t) * H + lane] = make_float2(cs[lane], sn[lane]);
+        if (!shared || a == 0)
+            table[table_row(p, a, t) * H + lane] = make_float2(cs[lane], sn[lane]);
     }
+    if (!store)
+        return;
     __syncthreads();
     const size_t slot = (size_t)p.Hkv * D;
     const size_t dst = ((size_t)ch.row * p.C + pos) * slot;
@@ -163,7 +179,7 @@ __global__ __launch_bounds__(64) void k_prefill_readable(PrefillParams p, const 
     const int row = ch.row, last = ch.s + t;
     const int kv = hq / p.G;
     const uint16_t *qs = p.q + a * p.q_sa + t * p.q_st + hq * p.q_sh;
-    const float2 *tab = table + ((size_t)a * p.T + t) * H;
+    const float2 *tab = table + table_row(p, a, t) * H;
     float q[D / 64];
     if (D == 128) {
         const float2 cs = tab[lane];
@@ -374,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                 x[ks][2 * e + 1] = E::hi(v[e]);
             }
         }
-        const float2 *cs = table + ((size_t)a * p.T + tq) * (D / 2);
+        const float2 *cs = table + table_row(p, a, tq) * (D / 2);
 #pragma unroll
         for (int ks = 0; ks < KS / 2; ++ks)
 #pragma unroll
@@ -418,26 +434,29 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
         const int k0 = t * BN;
         // some key of the tile is visible to one of this wave's queries, and the
         // wave holds at least one query of the entry
-        if (k0 <= s0 + qw + 31 && qw < n) {
+        // NBLK live 32-key blocks of the tile: 2, or 1 on the causal diagonal
+        // when the tile's second block lies past every query of the wave
+        auto body = [&](auto nblk) {
+            constexpr int NBLK = decltype(nblk)::value;
             const unsigned char *kt = buf ? klds1 : klds0, *vt = buf ? vlds1 : vlds0;
-            // two independent 32-key blocks per k-step, so each fragment read
+            // independent 32-key blocks per k-step, so each fragment read
             // overlaps the other block's product
-            f32x16 st[2];
+            f32x16 st[NBLK];
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NBLK; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     st[b][i] = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                u32x4 kf[2];
+                u32x4 kf[NBLK];
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < NBLK; ++b)
                     kf[b] = *(const u32x4 *)(kt + koff[ks] + b * 32 * ROW);
 #pragma unroll
                 for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-                    for (int b = 0; b < 2; ++b)
+                    for (int b = 0; b < NBLK; ++b)
                         st[b] = E::mma32(__builtin_bit_cast(vec8, kf[b]), bq[pp][ks], st[b]);
             }
             // raw scores; the scale (> 0) is applied inside exp2 below, so the max
@@ -448,7 +467,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                 // key k0 + 4 hh + rel is visible to query qrow iff rel <= lim
                 const int lim = s0 + qrow - k0 - 4 * hh;
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < NBLK; ++b)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int rel = b * 32 + 8 * (i >> 2) + (i & 3);
@@ -456,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                     }
             }
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NBLK; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     tmax = fmaxf(tmax, st[b][i]);
@@ -480,9 +499,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                     O[db] *= alpha;
                 m_run = m_new;
             }
-            vec8 pb[4];
+            vec8 pb[2 * NBLK];
 #pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) {
+            for (int k2 = 0; k2 < 2 * NBLK; ++k2) {
                 u32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -501,7 +520,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
             }
             // PV: slot j of k-step k2 is key 32 (k2 / 2) + 16 (k2 % 2) + 8 (j / 4) + 4 hh + j % 4
 #pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) {
+            for (int k2 = 0; k2 < 2 * NBLK; ++k2) {
                 const int rows_k2 = (32 * (k2 >> 1) + 16 * (k2 & 1)) * ROW;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
@@ -513,6 +532,12 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                     O[db] = E::mma32(__builtin_bit_cast(vec8, vv), pb[k2], O[db]);
                 }
             }
+        };
+        if (k0 <= s0 + qw + 31 && qw < n) {
+            if (k0 + 32 > s0 + qw + 31)
+                body(Buf<1>{});
+            else
+                body(Buf<2>{});
         }
         __builtin_amdgcn_s_waitcnt(0);  // the next tile's DMA (this wave's share)
         __syncthreads();                // ... and every wave's; buffer buf is free again
