@@ -71,6 +71,13 @@ def parse():
                     help="layer caches rotated in the ragged and long-context legs")
     ap.add_argument("--ceiling-reps", type=int, default=5,
                     help="timed reads per launch shape of the streaming-read ceiling (0 = skip)")
+    ap.add_argument("--fold-counters", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
+                    help="fold two rocprofv3 --pmc counter_collection.csv files of one bench leg "
+                         "(FETCH_SIZE, then WRITE_SIZE) into profiles/counters.json under the "
+                         "workload's label, scaled by the copy reference, and exit")
+    ap.add_argument("--fold-copy", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="fold the two counter runs of --copy-reference (the scale of "
+                         "FETCH_SIZE and WRITE_SIZE) into profiles/counters.json, and exit")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times): the reference that "
                          "scales the HBM byte counters of a profiler run")
@@ -154,6 +161,75 @@ def measured_traffic(kernel, workload):
     return e.get("hbm_bytes_per_launch")
 
 
+def _counter_means(path, counter):
+    """Mean value per dispatch of `counter`, by short kernel name (k_* kernels and
+    the runtime's copy kernel), from a rocprofv3 counter_collection.csv."""
+    import csv
+    import re
+    sums, counts = {}, {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            m = re.search(r"\b(k_[a-z0-9_]+|__amd_rocclr_copyBuffer)\b", r["Kernel_Name"])
+            if not m:
+                continue
+            k = m.group(1)
+            sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+            counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def _load_counters():
+    try:
+        with open(COUNTERS) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return {"kernels": {}}
+
+
+def _save_counters(c):
+    with open(COUNTERS, "w") as f:
+        json.dump(c, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
+def fold_copy(fetch_csv, write_csv):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the 1 GiB device copy of
+    --copy-reference: their ratio to the bytes copied scales every kernel's
+    counters to bytes."""
+    n = 1 << 30
+    fk = _counter_means(fetch_csv, "FETCH_SIZE")["__amd_rocclr_copyBuffer"]
+    wk = _counter_means(write_csv, "WRITE_SIZE")["__amd_rocclr_copyBuffer"]
+    c = _load_counters()
+    c["copy_reference"] = {"bytes": n, "fetch_kib": fk, "write_kib": wk,
+                           "fetch_scale": n / (fk * 1024.0), "write_scale": n / (wk * 1024.0)}
+    _save_counters(c)
+    print(json.dumps(c["copy_reference"]))
+
+
+def fold_counters(label, fetch_csv, write_csv):
+    """HBM bytes per launch of the k_* kernels of one workload's bench leg:
+    FETCH_SIZE and WRITE_SIZE means, each scaled by the copy reference, stored
+    with the digest of the kernel family's sources (used only while it matches)."""
+    c = _load_counters()
+    ref = c.get("copy_reference")
+    assert ref, "fold the copy reference first (--fold-copy)"
+    family = "decode" if label.endswith("decode") or "_decode_" in label else "prefill"
+    fetch, write = _counter_means(fetch_csv, "FETCH_SIZE"), _counter_means(write_csv, "WRITE_SIZE")
+    for k in sorted(set(fetch) & set(write)):
+        if not k.startswith("k_" + family):
+            continue
+        fb = fetch[k] * 1024.0 * ref["fetch_scale"]
+        wb = write[k] * 1024.0 * ref["write_scale"]
+        c["kernels"][f"{k}@{label}"] = {
+            "source_digest": source_digest(family), "fetch_kib_raw": fetch[k],
+            "write_kib_raw": write[k], "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
+            "hbm_bytes_per_launch": int(round(fb + wb))}
+        print(k, label, c["kernels"][f"{k}@{label}"])
+    _save_counters(c)
+
+
 def copy_reference():
     import torch
     n = 1 << 30
@@ -167,6 +243,12 @@ def copy_reference():
 
 def main():
     args = parse()
+    if args.fold_copy:
+        fold_copy(*args.fold_copy)
+        return
+    if args.fold_counters:
+        fold_counters(*args.fold_counters)
+        return
     if args.copy_reference:
         copy_reference()
         return
