@@ -78,6 +78,13 @@ def parse():
     ap.add_argument("--fold-copy", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="fold the two counter runs of --copy-reference (the scale of "
                          "FETCH_SIZE and WRITE_SIZE) into profiles/counters.json, and exit")
+    ap.add_argument("--phases", action="store_true",
+                    help="per-phase timeline of the decode stream kernel on --workload from "
+                         "per-group wall-clock stamps (needs the stamps build: python -m "
+                         "positions_aware_cached_amd.build --stamps); one JSON line")
+    ap.add_argument("--trace-phases", metavar="KERNEL_TRACE_CSV",
+                    help="stream kernel, merge kernel and the gaps between them, from a "
+                         "rocprofv3 --kernel-trace CSV of a decode bench run; one JSON line")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times): the reference that "
                          "scales the HBM byte counters of a profiler run")
@@ -97,6 +104,20 @@ def hip_runtime():
                 L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
                 return L
     raise RuntimeError("HIP runtime not loaded")
+
+
+# HIP event flag: no system-scope fence (cache writeback and invalidation) when
+# the event is recorded.  The bench's events only time kernels and are read
+# after a device-wide synchronize, so the fence buys nothing and, on MI355X,
+# delays the work queued after the event's kernel by several microseconds.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+TIMING_EVENT_FLAGS = HIP_EVENT_DISABLE_SYSTEM_FENCE
+
+
+def timing_event(hip, h):
+    """Create a timing event into the c_void_p h; returns the HIP status."""
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    return hip.hipEventCreateWithFlags(ctypes.byref(h), TIMING_EVENT_FLAGS)
 
 
 def percentile(xs, q):
@@ -230,6 +251,133 @@ def fold_counters(label, fetch_csv, write_csv):
     _save_counters(c)
 
 
+def decode_phases(args, calls=24):
+    """Timeline of the decode stream kernel, per launch, from the stamps build:
+    each work group records the wall clock (100 MHz) at entry, when its plan is
+    known, when its first tile has landed and at exit.  Times are in us from the
+    earliest group entry of the launch; the kernel's own duration comes from HIP
+    events around its dispatch.  Phases (medians over the launches):
+      start     event duration minus (last exit - first entry): dispatch, first
+                wave start and drain after the last wave;
+      plan      median group time from entry to a known first tile;
+      ramp      median (and max) first tile landed: all groups request their
+                first tiles at once, so this is the time HBM takes to serve them;
+      steady    from the median first tile to the 10th-percentile group exit;
+      tail      10th-percentile to last group exit (groups finishing unevenly)."""
+    import torch
+
+    from positions_aware_cached_amd import build as pbuild
+    import positions_aware_cached_amd as pac
+    import workloads
+
+    if not os.path.exists(pbuild.STAMPS_LIB):
+        sys.exit("bench.py --phases needs the stamps build: "
+                 "python -m positions_aware_cached_amd.build --stamps")
+    L = pac.load(pbuild.STAMPS_LIB)
+    L.mllm_debug_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    hip = hip_runtime()
+    dev = torch.device("cuda:0")
+    cfg = decode_config(args, "bf16")
+    A, Hq, D = cfg["A"], cfg["Hq"], cfg["D"]
+    inp = workloads.draw_decode(cfg, device="cuda")
+    nl = max(1, args.layers)
+    layers = [(inp["Kc"], inp["Vc"])] + workloads.draw_cache_layers(cfg, nl - 1)
+    cache = pac.Cache.wrap([k for k, _ in layers], [v for _, v in layers])
+    pos = torch.as_tensor(inp["positions"], device=dev)
+    rows = torch.as_tensor(inp["rows"], device=dev)
+    out = torch.empty((A, Hq, D), dtype=inp["q"].dtype, device=dev)
+    mirror = np.concatenate([inp["positions"], inp["rows"]]).astype(np.int32)
+    ws = torch.zeros(pac.decode_workspace_size(cache, A, Hq, int(inp["positions"].max())),
+                     dtype=torch.uint8, device=dev)
+    call = pac.DecodeCall(cache, inp["q"], inp["k_new"], inp["v_new"], pos, rows, out, ws,
+                          cfg["base"], host_mirror=mirror)
+    for i in range(max(args.warmup, nl)):
+        call(i % nl)
+    torch.cuda.synchronize()
+    nslot = 4096 * 8
+    rec = {k: [] for k in ("event", "start", "plan", "ramp_med", "ramp_max", "steady",
+                           "tail", "exit_p10", "exit_med", "exit_max")}
+    groups = 0
+    for i in range(calls):
+        pair = (ctypes.c_void_p * 2)()
+        for j in range(2):
+            h = ctypes.c_void_p()
+            assert timing_event(hip, h) == 0
+            pair[j] = h.value
+        st = np.zeros(nslot, dtype=np.uint64)
+        call(i % nl, attn_events=pair)
+        torch.cuda.synchronize()
+        assert L.mllm_debug_stamps(st.ctypes.data, st.nbytes) == 0
+        f = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(pair[0]),
+                                       ctypes.c_void_p(pair[1])) == 0
+        for j in range(2):
+            hip.hipEventDestroy(ctypes.c_void_p(pair[j]))
+        g = st.reshape(4096, 8)
+        g = g[(g[:, 0] > 0) & (g[:, 3] >= g[:, 0])].astype(np.int64)
+        # only the groups of this launch: exits after its earliest entry
+        t0 = g[:, 0].min()
+        g = g[g[:, 3] >= t0]
+        groups = len(g)
+        rel = (g - t0) * 0.01
+        ev = f.value * 1e3
+        ex = rel[:, 3]
+        rec["event"].append(ev)
+        rec["start"].append(ev - ex.max())
+        rec["plan"].append(float(np.median(rel[:, 1])))
+        rec["ramp_med"].append(float(np.median(rel[:, 7])))
+        rec["ramp_max"].append(float(rel[:, 7].max()))
+        rec["exit_p10"].append(float(np.percentile(ex, 10)))
+        rec["exit_med"].append(float(np.median(ex)))
+        rec["exit_max"].append(float(ex.max()))
+        rec["steady"].append(rec["exit_p10"][-1] - rec["ramp_med"][-1])
+        rec["tail"].append(rec["exit_max"][-1] - rec["exit_p10"][-1])
+    res = {"workload": decode_label(args), "launches": calls, "groups": groups,
+           "unit": "us", "source": "per-group wall-clock stamps (stamps build)"}
+    for k, v in rec.items():
+        res[k] = round(float(np.median(v)), 2)
+    print(json.dumps(res))
+
+
+def trace_phases(path):
+    """From a rocprofv3 kernel trace of a decode bench run, over back-to-back
+    steps (stream kernel, merge kernel, next stream kernel less than 50 us
+    apart): the stream and merge kernels' durations, the share of steps whose
+    kernels run with no gap between them (under 1 us), and the gaps of the
+    other steps: those that carry timing events (every few steps of the timed
+    loop; each event pair delays the work behind it) and the per-step
+    distribution pass.  Medians in us."""
+    import csv
+    import re
+    ks = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            m = re.search(r"\b(k_decode_[a-z_]+)\b", r["Kernel_Name"])
+            if m:
+                ks.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), m.group(1)))
+    ks.sort()
+    stream, merge, g1s, g2s, free = [], [], [], [], 0
+    for i in range(len(ks) - 2):
+        (s0, e0, n0), (s1, e1, n1), (s2, e2, n2) = ks[i], ks[i + 1], ks[i + 2]
+        if n0 != "k_decode_stream" or not n1.startswith("k_decode_merge") or n2 != n0:
+            continue
+        g1, g2 = (s1 - e0) / 1e3, (s2 - e1) / 1e3
+        if g1 > 50 or g2 > 50:
+            continue
+        stream.append((e0 - s0) / 1e3)
+        merge.append((e1 - s1) / 1e3)
+        if g1 < 1 and g2 < 1:
+            free += 1
+        else:
+            g1s.append(g1)
+            g2s.append(g2)
+    med = lambda x: round(float(np.median(x)), 2) if x else None
+    print(json.dumps({"unit": "us", "steps": len(stream), "stream": med(stream),
+                      "merge": med(merge), "gap_free_steps": free,
+                      "steps_with_gaps": len(g1s), "gap_to_merge": med(g1s),
+                      "gap_to_next_step": med(g2s), "source": os.path.basename(path)}))
+
+
 def copy_reference():
     import torch
     n = 1 << 30
@@ -251,6 +399,12 @@ def main():
         return
     if args.copy_reference:
         copy_reference()
+        return
+    if args.trace_phases:
+        trace_phases(args.trace_phases)
+        return
+    if args.phases:
+        decode_phases(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -399,7 +553,7 @@ def decode_leg(args, hip, dtype, K, W, L):
         pair = (ctypes.c_void_p * 2)()
         for j in range(2):
             h = ctypes.c_void_p()
-            assert hip.hipEventCreate(ctypes.byref(h)) == 0
+            assert timing_event(hip, h) == 0
             pair[j] = h.value
         evs[i] = pair
 
@@ -655,7 +809,7 @@ def bench_prefill(args, hip, name, K, dtype="bf16"):
         pair = (ctypes.c_void_p * 2)()
         for j in range(2):
             h = ctypes.c_void_p()
-            assert hip.hipEventCreate(ctypes.byref(h)) == 0
+            assert timing_event(hip, h) == 0
             pair[j] = h.value
         evs.append(pair)
 

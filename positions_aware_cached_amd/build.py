@@ -28,6 +28,10 @@ def sources():
 
 PROBE_SRC = os.path.join(HERE, "probe", "read_ceiling.hip")
 PROBE_LIB = os.path.join(HERE, "libreadprobe.so")
+# diagnosis build: the same library with the decode kernel's per-group wall-clock
+# stamps compiled in (MLLM_STAMPS; read back with mllm_debug_stamps), loaded only
+# by `bench.py --phases`
+STAMPS_LIB = os.path.join(HERE, "libmllm_stamps.so")
 
 
 def build(out=LIB, verbose=False, jobs=8):
@@ -83,5 +87,21 @@ def _wait(procs):
         raise RuntimeError("HIP build failed: " + ", ".join(os.path.basename(s) for s, _ in failed))
 
 
+def build_stamps(verbose=False, jobs=8):
+    """The library with MLLM_STAMPS defined, as STAMPS_LIB."""
+    global COMMON
+    saved = COMMON
+    COMMON = COMMON + ["-DMLLM_STAMPS"]
+    tmpdir = tempfile.mkdtemp(prefix="mllm_build_")
+    try:
+        return _build_in(sources(), tmpdir, STAMPS_LIB, verbose, jobs)
+    finally:
+        COMMON = saved
+        shutil.rmtree(tmpdir, ignore_errors=True)
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--stamps" in sys.argv:
+        print(build_stamps(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
