@@ -296,7 +296,8 @@ def decode_phases(args, calls=24):
     torch.cuda.synchronize()
     nslot = 4096 * 8
     rec = {k: [] for k in ("event", "start", "plan", "ramp_med", "ramp_max", "steady",
-                           "tail", "exit_p10", "exit_med", "exit_max")}
+                           "tail", "exit_p10", "exit_med", "exit_max", "exit_first_half",
+                           "exit_second_half", "exit_sd_first_half", "exit_sd_second_half")}
     groups = 0
     for i in range(calls):
         pair = (ctypes.c_void_p * 2)()
@@ -313,12 +314,17 @@ def decode_phases(args, calls=24):
                                        ctypes.c_void_p(pair[1])) == 0
         for j in range(2):
             hip.hipEventDestroy(ctypes.c_void_p(pair[j]))
-        g = st.reshape(4096, 8)
-        g = g[(g[:, 0] > 0) & (g[:, 3] >= g[:, 0])].astype(np.int64)
-        # only the groups of this launch: exits after its earliest entry
-        t0 = g[:, 0].min()
-        g = g[g[:, 3] >= t0]
+        g = st.reshape(4096, 8).astype(np.int64)
+        # only the groups of this launch: entries before their exits, exits
+        # after the launch's earliest entry (stale slots of larger launches)
+        live = (g[:, 0] > 0) & (g[:, 3] >= g[:, 0])
+        t0 = g[live, 0].min()
+        live &= g[:, 3] >= t0
+        idx = np.nonzero(live)[0]
+        g = g[live]
         groups = len(g)
+        # groups w < NS / 2 are each compute unit's first-dispatched group
+        first = idx < (idx.max() + 1) // 2
         rel = (g - t0) * 0.01
         ev = f.value * 1e3
         ex = rel[:, 3]
@@ -330,6 +336,10 @@ def decode_phases(args, calls=24):
         rec["exit_p10"].append(float(np.percentile(ex, 10)))
         rec["exit_med"].append(float(np.median(ex)))
         rec["exit_max"].append(float(ex.max()))
+        rec["exit_first_half"].append(float(np.mean(ex[first])))
+        rec["exit_second_half"].append(float(np.mean(ex[~first])))
+        rec["exit_sd_first_half"].append(float(np.std(ex[first])))
+        rec["exit_sd_second_half"].append(float(np.std(ex[~first])))
         rec["steady"].append(rec["exit_p10"][-1] - rec["ramp_med"][-1])
         rec["tail"].append(rec["exit_max"][-1] - rec["exit_p10"][-1])
     res = {"workload": decode_label(args), "launches": calls, "groups": groups,
