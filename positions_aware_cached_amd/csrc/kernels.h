@@ -8,6 +8,7 @@
 namespace mllm {
 
 constexpr int kMaxHalfDim = 64;  // D / 2 for the largest supported head size (128)
+constexpr int kMaxPrefillOrder = 256;  // entries a prefill schedule can reorder
 
 // Everything one decode step needs, resolved and validated by the host layer.
 struct DecodeParams {
@@ -76,7 +77,15 @@ struct PrefillParams {
     int32_t A, T, S, C, Hq, Hkv, D, G;
     float scale_log2;
     float inv_freq[kMaxHalfDim];
+    // the order in which the matrix-core kernel takes the entries (a schedule
+    // only): heaviest first for a chunk of mixed starts and lengths, so no long
+    // cached prefix starts last; n_order = 0 takes them in index order
+    int32_t n_order;
+    uint16_t order[kMaxPrefillOrder];
 };
+// fills p.n_order / p.order from the host copies of the chunk's starts and
+// lengths (starts == NULL: the equal-length prefill, index order)
+void prefill_order(PrefillParams &p, const int32_t *starts_host, const int32_t *lens_host);
 uint64_t prefill_workspace_bytes(int64_t A, int64_t T, int64_t Hq, int64_t D);
 // RoPE(K) + K/V store, then attention: kernel 0 = matrix-core tiles, 1 = readable.
 // e0 / e1: optional events stamped at the attention kernel's start and end.

@@ -906,6 +906,7 @@ mllm_status prefill_call(mllm_cache *cache, int32_t layer, const mllm_tensor_vie
     p.dtype = d.dtype;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     fill_inv_freq(p.inv_freq, rope->base, D);
+    mllm::prefill_order(p, chunk ? chunk_host : nullptr, chunk ? chunk_host + A : nullptr);
     hipEvent_t *ev = opts ? (hipEvent_t *)opts->attn_events : nullptr;
     hipError_t e = mllm::launch_prefill(p, (hipStream_t)stream, kernel, ev ? ev[0] : nullptr,
                                         ev ? ev[1] : nullptr);

@@ -15,7 +15,9 @@
 //                       writes the FP32 cos/sin table row of its position (one
 //                       row per position in an equal-length prefill).
 //   k_prefill_mfma      the tuned attention: one workgroup of four waves per
-//                       (entry, query head, 128-query tile), FlashAttention-
+//                       (entry, four query heads of a kv head, 32-query tile;
+//                       fewer heads and longer tiles when G is not a multiple
+//                       of four), FlashAttention-
 //                       style online softmax over 64-key tiles on the matrix
 //                       cores (see below).
 //   k_prefill_readable  one wave per (entry, token, query head), keys one at a
@@ -23,6 +25,10 @@
 //                       diagnosis).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <utility>
+#include <vector>
 
 #include "elem.h"
 #include "kernels.h"
@@ -239,8 +245,17 @@ struct Buf {
     static constexpr int value = B;
 };
 //
-// One workgroup (4 waves, wave w owns queries q0 + 32 w .. + 31) per (entry a,
-// query head hq, query tile q0 .. q0 + 127); the kv head is hq / G.  Key tiles
+// Query heads of one kv head that share a matrix-core work group: four when G
+// allows, else two or one; the four waves cover HB heads times 4 / HB
+// sub-tiles of 32 query positions.
+__host__ __device__ __forceinline__ int heads_per_block(int G)
+{
+    return (G & 3) == 0 ? 4 : ((G & 1) == 0 ? 2 : 1);
+}
+
+// One workgroup of 4 waves per (entry a, kv head, group of HB query heads,
+// query tile q0 .. q0 + 128 / HB - 1): wave w owns query head HB g + w % HB of
+// the kv head's G and queries q0 + 32 (w / HB) .. + 31.  Key tiles
 // of 64 move from memory straight into two LDS buffers by LDS-DMA (the next
 // tile while the current one is computed), each key row's 16-byte chunks
 // permuted by swz.  Per tile and wave:
@@ -271,7 +286,12 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     constexpr int NI = BN / RPI;            // DMA instructions per tile and tensor
     constexpr float HEADROOM = 8.0f;
 
-    const int nqt = (p.T + BM - 1) / BM;
+    // The four waves hold HB query heads of one kv head times 4 / HB sub-tiles of
+    // 32 query positions (HB = 4 whenever G allows): with four heads at the same
+    // positions every wave has the same causal extent, so no wave idles through
+    // the block's last key tiles while the others finish the diagonal.
+    const int HB = heads_per_block(p.G), BQ = BM / HB, nhb = p.G / HB;
+    const int nqt = (p.T + BQ - 1) / BQ;
     // Work groups are handed to the eight XCDs in turn (group b to XCD b % 8),
     // and each XCD has its own L2.  The G query heads and all query tiles of a kv
     // head read the same K/V tiles, so all blocks of one (entry, kv head) pair go
@@ -279,32 +299,42 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     // PG, so that the K/V rows in use at once fit its L2 (all of an XCD's pairs
     // at once did not: every tile was fetched several times), and runs a chunk's
     // blocks longest query tile first (the tile rank is the slowest index within
-    // the chunk), its pairs and heads within a rank.
-    int qt, hq, a;
+    // the chunk), its pairs and head groups within a rank.  Inside an XCD the
+    // dispatcher deals consecutive groups to its shader engines in turn, so the
+    // order of the pairs within a rank rotates by one per rank: one pair's blocks
+    // spread over the engines, and a pair with a long cached prefix (a chunk at a
+    // late start) does not load one engine with all its long blocks.
+    int qt, hg, a, kv;
     {
         const int b = blockIdx.x, npairs = p.A * p.Hkv;
+        int pair, rank, rem;
         if ((npairs & 7) == 0) {
             constexpr int PG = 4;
             const int ppx = npairs >> 3;  // pairs per XCD
             const int x = b & 7, j = b >> 3;
-            const int cb = PG * p.G * nqt;  // blocks of a full chunk of PG pairs
+            const int cb = PG * nhb * nqt;  // blocks of a full chunk of PG pairs
             const int c = j / cb, jj = j - c * cb;
-            const int per = min(PG, ppx - c * PG) * p.G;  // blocks of one tile rank in the chunk
-            const int rank = jj / per, rem = jj - rank * per;
-            const int pair = (c * PG + rem / p.G) * 8 + x;
-            a = pair / p.Hkv;
-            hq = (pair - a * p.Hkv) * p.G + rem % p.G;
-            qt = nqt - 1 - rank;
+            const int per = min(PG, ppx - c * PG) * nhb;  // blocks of one tile rank in the chunk
+            rank = jj / per;
+            rem = (jj - rank * per + rank) % per;
+            pair = (c * PG + rem / nhb) * 8 + x;
         } else {
-            const int per = p.Hq * p.A, rank = b / per, rem = b - rank * per;
-            a = rem / p.Hq;
-            hq = rem - a * p.Hq;
-            qt = nqt - 1 - rank;
+            const int per = npairs * nhb;
+            rank = b / per;
+            rem = (b - rank * per + rank) % per;
+            pair = rem / nhb;
         }
+        a = pair / p.Hkv;
+        kv = pair - a * p.Hkv;
+        if (a < p.n_order)
+            a = p.order[a];
+        hg = rem % nhb;
+        qt = nqt - 1 - rank;
     }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int qi = lane & 31, hh = lane >> 5;
-    const int q0 = qt * BM, qw = q0 + w * 32, qrow = qw + qi;
+    const int hq = kv * p.G + hg * HB + w % HB;  // this wave's query head
+    const int q0 = qt * BQ, qw = q0 + 32 * (w / HB), qrow = qw + qi;
     const Chunk ch = chunk_of(p, a);
     if (!ch.ok) {  // device values disagree with the checked host copy: NaN output
         if (qrow < p.T && hh == 0)
@@ -315,10 +345,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     if (q0 >= ch.n)
         return;  // the whole query tile lies past this entry's length
     const int row = ch.row, s0 = ch.s, n = ch.n;
-    const int kv = hq / p.G;
     // keys 0 .. s0 + n - 1 exist (the cached prefix and the chunk); the tile's
-    // last query sees up to key s0 + min(q0 + BM, n) - 1
-    const int nkeys = s0 + min(q0 + BM, n);
+    // last query sees up to key s0 + min(q0 + BQ, n) - 1
+    const int nkeys = s0 + min(q0 + BQ, n);
     const int ntiles = (nkeys + BN - 1) / BN;
 
     // K and V tiles, double-buffered, filled straight from memory by LDS-DMA.
@@ -570,6 +599,28 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
 
 }  // namespace
 
+void prefill_order(PrefillParams &p, const int32_t *starts_host, const int32_t *lens_host)
+{
+    p.n_order = 0;
+    if (!starts_host || p.A > kMaxPrefillOrder)
+        return;
+    // key tiles of one (entry, kv head, head group): the kernel's blocks of BQ
+    // queries, block j seeing keys up to s + min((j + 1) BQ, n) - 1
+    const int BQ = 128 / heads_per_block(p.G);
+    std::vector<std::pair<long long, int>> w(p.A);
+    for (int a = 0; a < p.A; ++a) {
+        const long long s = starts_host[a], n = lens_host[a];
+        long long tiles = 0;
+        for (long long q0 = 0; q0 < n; q0 += BQ)
+            tiles += (s + std::min(q0 + BQ, n) + 63) / 64;
+        w[a] = {-tiles, a};
+    }
+    std::stable_sort(w.begin(), w.end());
+    for (int a = 0; a < p.A; ++a)
+        p.order[a] = (uint16_t)w[a].second;
+    p.n_order = p.A;
+}
+
 uint64_t prefill_workspace_bytes(int64_t A, int64_t T, int64_t Hq, int64_t D)
 {
     (void)Hq;
@@ -590,7 +641,8 @@ static void launch_prefill_e(const PrefillParams &p, hipStream_t stream, int ker
             hipExtLaunchKernelGGL((k_prefill_readable<E, 128>), grid, dim3(64), 0, stream, e0, e1, 0,
                                   p, table);
     } else {
-        const dim3 grid(p.Hq * p.A * ((p.T + 127) / 128));
+        const int hb = heads_per_block(p.G);
+        const dim3 grid(p.Hq / hb * p.A * ((p.T + 128 / hb - 1) / (128 / hb)));
         if (p.D == 64)
             hipExtLaunchKernelGGL((k_prefill_mfma<E, 64>), grid, dim3(256), 0, stream, e0, e1, 0, p,
                                   table);
