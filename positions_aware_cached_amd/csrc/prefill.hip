@@ -79,10 +79,19 @@ struct Chunk {
 };
 __device__ __forceinline__ Chunk chunk_of(const PrefillParams &p, int a)
 {
+    // the three loads go out together, each from a device array (an absent
+    // one reads the row array instead and its value is dropped): one memory
+    // round trip
+    const int32_t *sp = p.starts ? p.starts : p.rows, *lp = p.lens ? p.lens : p.rows;
+    int rv = __builtin_amdgcn_readfirstlane(p.rows[a]);
+    int sv = __builtin_amdgcn_readfirstlane(sp[a]), lv = __builtin_amdgcn_readfirstlane(lp[a]);
+    // opaque to the compiler, so it neither waits for the row before issuing
+    // the other two nor folds the choice into one load's address
+    asm volatile("" : "+s"(rv), "+s"(sv), "+s"(lv));
     Chunk c;
-    c.row = p.rows[a];
-    c.s = p.starts ? p.starts[a] : 0;
-    c.n = p.lens ? p.lens[a] : p.T;
+    c.row = rv;
+    c.s = p.starts ? sv : 0;
+    c.n = p.lens ? lv : p.T;
     c.ok = c.row >= 0 && c.row < p.S && c.s >= 0 && c.n >= 1 && c.n <= p.T && c.s <= p.C - c.n;
     return c;
 }
@@ -353,11 +362,15 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     // K and V tiles, double-buffered, filled straight from memory by LDS-DMA.
     // Chunk c of key row r sits at chunk slot c ^ swz(r) of its LDS row, so the
     // operand reads below spread over all banks without padding.
-    // Four separate arrays, not one indexed by the buffer: accesses to distinct
-    // LDS variables are known not to alias, so the reads of one buffer need not
-    // wait for the memory-to-LDS loads into the other.
-    __shared__ __attribute__((aligned(16))) unsigned char klds0[BN * ROW], klds1[BN * ROW];
-    __shared__ __attribute__((aligned(16))) unsigned char vlds0[BN * ROW], vlds1[BN * ROW];
+    // Separate arrays per buffer, not one indexed by the buffer: accesses to
+    // distinct LDS variables are known not to alias, so the reads of one buffer
+    // need not wait for the memory-to-LDS loads into the other.  The second
+    // buffer's K and V tiles share one array (K, then V), which also stages the
+    // four waves' query rows before the first tile is in use.
+    __shared__ __attribute__((aligned(16))) unsigned char klds0[BN * ROW], vlds0[BN * ROW];
+    __shared__ __attribute__((aligned(16))) unsigned char kvlds1[2 * BN * ROW];
+    // cos/sin rows of the block's 32 positions when its four waves share them
+    __shared__ __attribute__((aligned(16))) unsigned char tlds[32 * D * 4];
 
     const size_t slot = (size_t)p.Hkv * D;
     const size_t rb = (size_t)row * p.C * slot + (size_t)kv * D;
@@ -370,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     // r = RPI i + l / CPR (clamped into the prompt) into slot l % CPR
     auto load_tile = [&](int t, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
-        unsigned char *kd = buf ? klds1 : klds0, *vd = buf ? vlds1 : vlds0;
+        unsigned char *kd = buf ? kvlds1 : klds0, *vd = buf ? kvlds1 + BN * ROW : vlds0;
 #pragma unroll
         for (int i = w; i < NI; i += 4) {
             const int r = i * RPI + lane / CPR;
@@ -407,26 +420,80 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
     // as two parts in the storage type (high part and rounded remainder)
     vec8 bq[2][KS];
     {
-        const int tq = min(qrow, n - 1);
-        const uint16_t *qs = p.q + a * p.q_sa + tq * p.q_st + hq * p.q_sh;
+        u32x4 qv[KS];
+        float4 cv[KS / 2][4];
+        if (HB == 4) {
+            // The four waves hold the same 32 positions: their query rows and the
+            // positions' cos/sin rows move by LDS-DMA, every instruction 1 KiB of
+            // whole rows (per-lane 16-B loads of 32 rows each touched 32 cache
+            // lines per instruction).  Wave w's query rows go to the second tile
+            // buffer (free until the first tile is in use) in the K tile layout,
+            // so the K operand offsets read them; the block's cos/sin rows go to
+            // tlds, chunk c of row r at slot c ^ swz(r).
+            const uint16_t *qb = p.q + a * p.q_sa + hq * p.q_sh;
+            unsigned char *qs = kvlds1 + w * 32 * ROW;
+#pragma unroll
+            for (int i = 0; i < 32 / RPI; ++i) {
+                const int r = i * RPI + lane / CPR;
+                const int c = ((lane % CPR) ^ swz(r)) & (CPR - 1);
+                lds_dma16(qb + (size_t)min(qw + r, n - 1) * p.q_st + c * 8, qs + i * 1024);
+            }
+            constexpr int CPT = D / 4;     // 16-B chunks of a cos/sin row
+            constexpr int RPT = 64 / CPT;  // cos/sin rows per DMA instruction
+#pragma unroll
+            for (int k = 0; k < 32 / RPT / 4; ++k) {  // a fixed count: no loop
+                const int i = w + 4 * k;
+                const int r = i * RPT + lane / CPT;
+                const int c = ((lane % CPT) ^ swz(r)) & (CPT - 1);
+                lds_dma16(table + table_row(p, a, min(q0 + r, n - 1)) * (D / 2) + c * 2,
+                          tlds + i * 1024);
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA; the barrier covers the others
+            __syncthreads();
+            const unsigned char *qd = kvlds1 + w * 32 * ROW;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qv[ks] = *(const u32x4 *)(qd + koff[ks]);
+#pragma unroll
+            for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    cv[ks][j] = *(const float4 *)(tlds + qi * (CPT * 16) +
+                                                  (((8 * ks + 4 * hh + j) ^ swz(qi)) << 4));
+        } else {
+            // waves at different positions: per-lane loads, both in flight before
+            // either is used (one memory round trip)
+            const int tq = min(qrow, n - 1);
+            const uint16_t *qs = p.q + a * p.q_sa + tq * p.q_st + hq * p.q_sh;
+            const float4 *cs = (const float4 *)(table + table_row(p, a, tq) * (D / 2));
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qv[ks] = *(const u32x4 *)(qs + ks * 16 + hh * 8);
+#pragma unroll
+            for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    cv[ks][j] = cs[ks * 8 + hh * 4 + j];
+            // everything is needed next anyway; waiting here also leaves no load
+            // pending where the two paths join
+            __builtin_amdgcn_s_waitcnt(0);
+        }
         float x[KS][8];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 v = *(const u32x4 *)(qs + ks * 16 + hh * 8);
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[ks][2 * e] = E::lo(v[e]);
-                x[ks][2 * e + 1] = E::hi(v[e]);
+                x[ks][2 * e] = E::lo(qv[ks][e]);
+                x[ks][2 * e + 1] = E::hi(qv[ks][e]);
             }
-        }
-        const float2 *cs = table + table_row(p, a, tq) * (D / 2);
 #pragma unroll
         for (int ks = 0; ks < KS / 2; ++ks)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float2 c = cs[ks * 16 + hh * 8 + j];
+                const float4 c4 = cv[ks][j >> 1];
+                const float c = (j & 1) ? c4.z : c4.x, sn = (j & 1) ? c4.w : c4.y;
                 float lo, hi;
-                rope_pair(x[ks][j], x[ks + KS / 2][j], c.x, c.y, lo, hi);
+                rope_pair(x[ks][j], x[ks + KS / 2][j], c, sn, lo, hi);
                 x[ks][j] = lo;
                 x[ks + KS / 2][j] = hi;
             }
@@ -467,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
         // when the tile's second block lies past every query of the wave
         auto body = [&](auto nblk) {
             constexpr int NBLK = decltype(nblk)::value;
-            const unsigned char *kt = buf ? klds1 : klds0, *vt = buf ? vlds1 : vlds0;
+            const unsigned char *kt = buf ? kvlds1 : klds0, *vt = buf ? kvlds1 + BN * ROW : vlds0;
             // independent 32-key blocks per k-step, so each fragment read
             // overlaps the other block's product
             f32x16 st[NBLK];
