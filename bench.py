@@ -30,7 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published
-EVENT_STRIDE = 4          # timed decode steps per step whose kernel carries HIP events
+EVENT_STRIDE = 10         # timed decode steps per step whose kernel carries HIP events
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak, published
 METRIC = "decode attn step: KV GB/s and % of HBM peak; tokens/s at A rows, ctx"
 
@@ -554,9 +554,10 @@ def decode_leg(args, hip, dtype, K, W, L):
     total_bytes = kv_bytes + io_bytes
 
     # The attention kernel's own duration: the library stamps start and end
-    # events into the dispatch of every EVENT_STRIDE-th timed step.  A stamped
-    # dispatch costs the step about 5 us more on MI355X (measured: 113.7 vs
-    # 118-120 us per Llama-like step), so the other steps run unstamped.
+    # events into the dispatch of every EVENT_STRIDE-th timed step (2 of the
+    # 20 timed steps of a short run, 20 of 200).  A stamped dispatch delays
+    # its step by about 9 us on MI355X (kernel trace: 4.5 us before the kernel,
+    # 4.5 us before the merge), so the other steps run unstamped.
     stamped = [i for i in range(K) if i % EVENT_STRIDE == EVENT_STRIDE - 1] or [K - 1]
     evs = {}
     for i in stamped:
