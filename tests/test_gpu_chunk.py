@@ -204,6 +204,31 @@ def test_chunks_in_sequence():
         assert ulp_dist(workloads.bits(Kc[r, :Ttot + 1]), Ko[r, :Ttot + 1]).max() <= 1
 
 
+@pytest.mark.parametrize("A,Hq,Hkv", [(256, 8, 2), (260, 8, 2), (257, 6, 2)],
+                         ids=["256_G4", "260_G4", "257_G3"])
+def test_chunk_many_entries(A, Hq, Hkv):
+    """More entries than the attention kernel's schedule takes heaviest first
+    (256): 256 entries still reordered, 257 and 260 in index order; four query
+    heads per work group (G = 4) and one (G = 3).  Every output and store of
+    every entry against the oracle."""
+    rng = np.random.default_rng(7000 + A + Hq)
+    T = 16
+    lens = rng.integers(1, T + 1, A).astype(np.int32)
+    lens[:3] = [1, T, T]
+    starts = rng.integers(0, 200, A).astype(np.int32)
+    starts[:3] = [0, 0, 190]
+    rows = rng.permutation(A + 2)[:A].astype(np.int32)
+    C = int((starts + lens).max()) + 5
+    cfg = workloads.config("prefill", A=A, S=A + 2, C=C, T=T, Hq=Hq, Hkv=Hkv, D=64,
+                           base=1.0e4, seed=7100 + A)
+    H.log(f"chunk many entries A={A} Hq={Hq} Hkv={Hkv}")
+    run = ChunkRun(cfg, starts, lens, rows)
+    Kpre, Vpre = run.Kc.clone(), run.Vc.clone()
+    run.run(0)
+    parity(run, Kpre, Vpre)
+    untouched(run, Kpre, Vpre)
+
+
 def test_chunk_full_config():
     """16 rows, chunks of 128..512 tokens at starts in [0, 3072], 32/8/128: every
     store checked, outputs of three entries at sampled queries checked against
