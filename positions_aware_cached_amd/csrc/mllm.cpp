@@ -796,9 +796,10 @@ mllm_status prefill_call(mllm_cache *cache, int32_t layer, const mllm_tensor_vie
     if ((st = resolve_opts(opts, &waves_unused, &kernel)))
         return st;
     // one-dimensional grids: the store kernel one 64-lane wave per (entry,
-    // token), the matrix-core kernel one 256-lane block per (entry, query head,
-    // 128 queries), the readable kernel one 64-lane wave per (entry, token,
-    // query head)
+    // token), the matrix-core kernel one 256-lane block per (entry, group of
+    // HB query heads, 128 / HB queries) -- at most one per (entry, query head,
+    // 128 queries), the bound checked here --, the readable kernel one 64-lane
+    // wave per (entry, token, query head)
     if (!grid_fits((int64_t)A * T, 64) ||
         (kernel == 1 ? !grid_fits((int64_t)A * T * Hq, 64)
                      : !grid_fits((int64_t)A * Hq * ((T + 127) / 128), 256)))
