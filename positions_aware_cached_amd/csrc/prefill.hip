@@ -497,17 +497,38 @@ __global__ __launch_bounds__(256, 2) void k_prefill_mfma(PrefillParams p, const 
                 x[ks][j] = lo;
                 x[ks + KS / 2][j] = hi;
             }
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
+        if constexpr (E::code == Bf16::code) {
+            // the same two parts as E::part<2>, two values per instruction: the
+            // high part is x with its low 16 bits cleared, the remainder x - hi
+            // (exact in FP32) goes through the hardware conversion, which rounds
+            // to nearest even like the storage type's own rounding
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                u32x4 v;
+                u32x4 vh, vl;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = E::template part<2>(x[ks][2 * e], pp) |
-                           (E::template part<2>(x[ks][2 * e + 1], pp) << 16);
-                bq[pp][ks] = __builtin_bit_cast(vec8, v);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t h0 = __float_as_uint(x[ks][2 * e]) & 0xffff0000u;
+                    const uint32_t h1 = __float_as_uint(x[ks][2 * e + 1]) & 0xffff0000u;
+                    vh[e] = (h0 >> 16) | h1;
+                    vl[e] = E::pack2(x[ks][2 * e] - __uint_as_float(h0),
+                                     x[ks][2 * e + 1] - __uint_as_float(h1));
+                }
+                bq[0][ks] = __builtin_bit_cast(vec8, vh);
+                bq[1][ks] = __builtin_bit_cast(vec8, vl);
             }
+        } else {
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    u32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = E::template part<2>(x[ks][2 * e], pp) |
+                               (E::template part<2>(x[ks][2 * e + 1], pp) << 16);
+                    bq[pp][ks] = __builtin_bit_cast(vec8, v);
+                }
+        }
     }
 
     f32x16 O[NDB];
