@@ -148,8 +148,9 @@ __global__ __launch_bounds__(64) void k_prefill_store(PrefillParams p, float2 *t
             float l0, h0, l1, h1;
             rope_pair(E::lo(x4[e]), E::lo(y4[e]), cs[i0], sn[i0], l0, h0);
             rope_pair(E::hi(x4[e]), E::hi(y4[e]), cs[i1], sn[i1], l1, h1);
-            lo4[e] = E::from_f(l0) | (E::from_f(l1) << 16);
-            hi4[e] = E::from_f(h0) | (E::from_f(h1) << 16);
+            // the packed conversion instruction: round to nearest even, two at a time
+            lo4[e] = E::pack2(l0, l1);
+            hi4[e] = E::pack2(h0, h1);
         }
         uint16_t *kd = p.kc + dst + (size_t)h * D + c * 8;
         *(u32x4 *)kd = lo4;
