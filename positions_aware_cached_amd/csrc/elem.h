@@ -65,8 +65,8 @@ struct Bf16 {
         if (p == 0)
             return h >> 16;
         const float r1 = x - __uint_as_float(h);
-        if (NPART == 2)
-            return from_f(r1);
+        if (NPART == 2)  // the conversion instruction: nearest even, as from_f
+            return __builtin_bit_cast(uint16_t, (__bf16)r1);
         const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
         if (p == 1)
             return mid >> 16;
