@@ -93,7 +93,7 @@ def untouched(run, Kpre, Vpre):
 
 SHAPES = [  # (T, Hq, Hkv, D)
     (1, 4, 2, 64), (17, 8, 2, 128), (64, 4, 4, 128), (65, 8, 2, 64), (128, 32, 8, 128),
-    (129, 8, 2, 128), (200, 6, 2, 64), (333, 16, 2, 128),
+    (129, 8, 2, 128), (200, 6, 2, 64), (333, 16, 2, 128), (97, 32, 2, 128),
 ]
 
 
