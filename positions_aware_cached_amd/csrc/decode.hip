@@ -183,10 +183,11 @@ __device__ __forceinline__ float wave_max(float v)
 // tiles of kTile keys; segments follow in entry-major order (seg = a * Hkv +
 // h), so segment (a, h) covers the global tiles [Hkv E(a) + h n(a), + n(a)),
 // where n(a) is entry a's tile count (0 for an entry whose position or row is
-// out of range) and E(a) = n(0) + ... + n(a - 1).  Wave w owns the global
-// tiles [t0(w), t0(w + 1)), t0(w) = floor(w NT / NW): every wave gets the same
-// number of tiles whatever the row lengths (with two groups per compute unit
-// the first-dispatched half gets a larger share, see plan_t0).  A wave
+// out of range) and E(a) = n(0) + ... + n(a - 1).  The plan splits the tiles,
+// and with short segments their starts too, into NW ranges of equal work
+// whatever the row lengths (with two groups per compute unit the
+// first-dispatched half gets a larger share, see make_plan); group w owns the
+// global tiles [t0(w), t0(w + 1)) that start in its range.  A wave
 // walks its range across segment boundaries, keeps the next tile in flight
 // across them, and writes one partial (reference max, sum, unnormalized
 // output of each of the G query heads) per segment it touches into slot
@@ -340,117 +341,100 @@ __device__ __forceinline__ void load_block(const Entries &p, int c0, int lane, E
         b.na[k] = tiles_of(p, c0 + 64 * k + lane, b.pos[k], b.row[k]);
 }
 
-// A block of entries with the inclusive scans of its tile counts: incl[k] on
-// lane l sums n(c0 + 64 k + i) for i <= l.
+// A block of entries with the inclusive scans of its tile counts and of its
+// valid entries: incl[k] on lane l sums n(c0 + 64 k + i) for i <= l, cnt[k]
+// counts the i <= l with n(c0 + 64 k + i) > 0.
 struct ScanBlock {
     EntryBlock b;
-    int incl[4];
+    int incl[4], cnt[4];
 };
 __device__ __forceinline__ void scan_block(const Entries &p, int c0, int lane, ScanBlock &s)
 {
     load_block(p, c0, lane, s.b);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < 4; ++k) {
         s.incl[k] = wave_incl_scan(s.b.na[k], lane);
+        // the ballot's bits below this lane, plus its own
+        const unsigned long long v = __ballot(s.b.na[k] > 0);
+        s.cnt[k] = __builtin_amdgcn_mbcnt_hi((unsigned)(v >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((unsigned)v, 0u)) +
+                   (s.b.na[k] > 0);
+    }
 }
 
-// NT = NHG * sum_a n(a), on every lane; the first block (entries 0..255) is
-// left in first, so that the plan's later passes need not read it again.
-__device__ long long plan_total(const Entries &p, int lane, ScanBlock &first)
+// Totals on every lane: NT = NHG * sum_a n(a) tiles in NSEG = NHG * #{a :
+// n(a) > 0} segments; the first block (entries 0..255) is left in first, so
+// that the plan's later passes need not read it again.
+struct Totals {
+    long long NT, NSEG;
+};
+__device__ Totals plan_total(const Entries &p, int lane, ScanBlock &first)
 {
     scan_block(p, 0, lane, first);
-    long long s = 0;
+    long long s = 0, c = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < 4; ++k) {
         s += __builtin_amdgcn_readlane(first.incl[k], 63);
+        c += __builtin_amdgcn_readlane(first.cnt[k], 63);
+    }
     for (int c0 = 256; c0 < p.A; c0 += 256) {
         ScanBlock sb;
         scan_block(p, c0, lane, sb);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            s += __builtin_amdgcn_readlane(sb.incl[k], 63);
-    }
-    return s * p.NHG;
-}
-
-// The entry holding global tile t < NT, NHG * E(entry), and the 64-entry chunk
-// around it (lane l: entry ec + l), on every lane.
-__device__ void plan_locate(const Entries &p, long long t, int lane, const ScanBlock &first,
-                            int &a_out, long long &base_out, int &ec, int &e_pos, int &e_row,
-                            int &e_na)
-{
-    long long run = 0;
-    for (int c0 = 0; c0 < p.A; c0 += 256) {
-        ScanBlock sb;
-        if (c0 == 0)
-            sb = first;
-        else
-            scan_block(p, c0, lane, sb);
-        const EntryBlock &b = sb.b;
-#pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int incl = sb.incl[k];
-            const long long end = run + (long long)p.NHG * incl;
-            const unsigned long long hit = __ballot(t < end && b.na[k] > 0);
-            if (hit) {
-                const int l = __ffsll((long long)hit) - 1;
-                a_out = c0 + 64 * k + l;
-                base_out = __shfl(end - (long long)p.NHG * b.na[k], l, 64);
-                ec = c0 + 64 * k;
-                e_pos = b.pos[k];
-                e_row = b.row[k];
-                e_na = b.na[k];
-                return;
-            }
-            run += (long long)p.NHG * __builtin_amdgcn_readlane(incl, 63);
+            s += __builtin_amdgcn_readlane(sb.incl[k], 63);
+            c += __builtin_amdgcn_readlane(sb.cnt[k], 63);
         }
     }
-    a_out = p.A;  // not reached for t < NT
-    base_out = run;
-    ec = 0;
-    e_pos = e_row = e_na = 0;
+    return Totals{s * p.NHG, c * p.NHG};
 }
 
-// Groups of the plan: min(launched, NT); group w owns the tiles
-// [t0(w), t0(w + 1)) (below), never an empty range.
+// Groups of the plan: min(launched, NT); group w owns the units
+// [v0(w), v0(w + 1)) (below), never an empty range, and with them the tiles
+// that start there (possibly none: a range of segment starts only).
 __device__ __forceinline__ int plan_waves(int launched, long long NT)
 {
     return (int)min((long long)launched, NT);
 }
 
-// First tile of group w.  With two resident groups per compute unit the
+// Plan units.  A tile is one unit of work.  When the segments are short (on
+// average under 32 tiles each) a segment's start -- its queries, cos/sin, the
+// store of the new token, the partial it writes -- costs about as much as a
+// tile and is one more unit (su = 1), laid out before the segment's tiles, so
+// a group that starts many segments gets fewer tiles; with long segments the
+// starts are a small share and the plan counts tiles only (su = 0, measured
+// as fast on MI355X).  Segment (a, h) of n(a) > 0 tiles is then u(a) = n(a) +
+// su units, and the NU = NT + su NSEG units are split as follows.
+//
+// First unit of group w.  With two resident groups per compute unit the
 // groups of the first half are each unit's first-dispatched group, whose waves
-// win the instruction-issue ties of their SIMDs and run ahead.  When the
-// segments are long (at least 32 tiles each on average), a group's time
-// follows its tile count, and the first half gets weight plan_wa, the second
-// plan_wb: t0(w) = floor(W(w) NT / W(NW)), W the running weight.  The host
-// picks the ratio by the work per tile (measured on MI355X with the K/V tiles
-// read non-temporally: 46 : 30 with up to 4 query heads per kv head, 41 : 28
-// with 5-16, the best of the ratios 1.37, 1.46, 1.53 and 1.60 on the
-// Llama-like and long-context batches).  With short segments the per-segment
-// work dominates and the tile weights measured no faster, so the split stays
-// uniform (weight 1 each), as it does when NW is odd or there are fewer than
-// four tiles per group (no range is empty).
-// The plan of a launch: NT tiles over NW groups, group w from tile t0(w) =
-// floor(W(w) NT / W(NW)) on, W the running weight (see above); computed once
-// and pinned in scalar registers.
+// win the instruction-issue ties of their SIMDs and run ahead, and the first
+// half gets weight plan_wa, the second plan_wb: v0(w) = floor(W(w) NU /
+// W(NW)), W the running weight.  The host picks the ratio by the work per
+// tile (measured on MI355X with the K/V tiles read non-temporally: 46 : 30
+// with up to 4 query heads per kv head, 41 : 28 with 5-16, the best of the
+// ratios 1.37, 1.46, 1.53 and 1.60 on the Llama-like and long-context
+// batches; with su = 1 the same ratio measured faster than a uniform split on
+// a ragged batch).  The split stays uniform (weight 1 each) when NW is odd or
+// there are fewer than four tiles per group (no range is empty).
+// The plan of a launch, computed once and pinned in scalar registers.
 struct Plan {
-    long long NT, WNW, wa, wb;
-    int NW, half;
-    int weighted;
+    long long NU, WNW, wa, wb;
+    int NW, half, su;
 };
-__device__ __forceinline__ Plan make_plan(const DecodeParams &p, long long NT, int NW)
+__device__ __forceinline__ Plan make_plan(const DecodeParams &p, long long NT, long long NSEG,
+                                          int NW)
 {
     Plan P;
-    P.NT = NT;
+    P.su = NT < 32ll * p.A * p.NHG ? 1 : 0;
+    P.NU = P.su ? NT + NSEG : NT;
     P.NW = NW;
     P.half = NW >> 1;
-    P.weighted = p.plan_weighted && !(NW & 1) && NT >= 4ll * NW &&
-                 NT >= 32ll * p.A * p.NHG;
-    P.wa = P.weighted ? p.plan_wa : 1;
-    P.wb = P.weighted ? p.plan_wb : 1;
+    const bool weighted = p.plan_weighted && !(NW & 1) && NT >= 4ll * NW;
+    P.wa = weighted ? p.plan_wa : 1;
+    P.wb = weighted ? p.plan_wb : 1;
     P.WNW = P.wa * P.half + P.wb * (NW - P.half);
-    pin(P.NT);
+    pin(P.NU);
     pin(P.WNW);
     pin(P.wa);
     pin(P.wb);
@@ -462,19 +446,88 @@ __device__ __forceinline__ long long plan_weight(const Plan &P, int w)
 {
     return w <= P.half ? P.wa * w : P.wa * P.half + P.wb * (w - P.half);
 }
-__device__ __forceinline__ long long plan_t0(const Plan &P, int w)
+__device__ __forceinline__ long long plan_v0(const Plan &P, int w)
 {
-    return plan_weight(P, w) * P.NT / P.WNW;
+    return plan_weight(P, w) * P.NU / P.WNW;
 }
 
-// Group that owns global tile t: the largest w with t0(w) <= t, i.e. with
-// W(w) <= X = floor(((t + 1) W(NW) - 1) / NT).
-__device__ __forceinline__ int plan_wave_of(const Plan &P, long long t)
+// Group that owns unit v: the largest w with v0(w) <= v, i.e. with
+// W(w) <= X = floor(((v + 1) W(NW) - 1) / NU).
+__device__ __forceinline__ int plan_wave_of(const Plan &P, long long v)
 {
-    const long long X = ((t + 1) * P.WNW - 1) / P.NT;
+    const long long X = ((v + 1) * P.WNW - 1) / P.NU;
     const long long C = P.half;
     const long long w = X <= P.wa * C ? X / P.wa : C + (X - P.wa * C) / P.wb;
     return (int)min(w, (long long)P.NW - 1);
+}
+
+// Units of an entry of na tiles, and of the scanned entries up to this lane.
+__device__ __forceinline__ int units_of(const Plan &P, int na) { return na + (na > 0 ? P.su : 0); }
+__device__ __forceinline__ int units_incl(const Plan &P, const ScanBlock &s, int k)
+{
+    return s.incl[k] + P.su * s.cnt[k];
+}
+
+// Where plan unit v < NU falls: its entry a and tile count na, the entry's
+// first tile (NHG * E(a)) and first unit, and the 64-entry chunk around it
+// (lane l: entry ec + l), on every lane.
+struct Located {
+    int a, na, ec, e_pos, e_row, e_na;
+    long long tbase, ubase;
+};
+__device__ Located plan_locate(const Entries &p, const Plan &P, long long v, int lane,
+                               const ScanBlock &first)
+{
+    long long run = 0, urun = 0;
+    for (int c0 = 0; c0 < p.A; c0 += 256) {
+        ScanBlock sb;
+        if (c0 == 0)
+            sb = first;
+        else
+            scan_block(p, c0, lane, sb);
+        const EntryBlock &b = sb.b;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int ui = units_incl(P, sb, k);
+            const long long uend = urun + (long long)p.NHG * ui;
+            const unsigned long long hit = __ballot(v < uend && b.na[k] > 0);
+            if (hit) {
+                const int l = __ffsll((long long)hit) - 1;
+                Located r;
+                r.a = c0 + 64 * k + l;
+                r.na = __builtin_amdgcn_readlane(b.na[k], l);
+                r.tbase = run + (long long)p.NHG * __builtin_amdgcn_readlane(sb.incl[k] - r.na, l);
+                r.ubase = urun + (long long)p.NHG *
+                                     __builtin_amdgcn_readlane(ui - units_of(P, r.na), l);
+                r.ec = c0 + 64 * k;
+                r.e_pos = b.pos[k];
+                r.e_row = b.row[k];
+                r.e_na = b.na[k];
+                return r;
+            }
+            run += (long long)p.NHG * __builtin_amdgcn_readlane(sb.incl[k], 63);
+            urun += (long long)p.NHG * __builtin_amdgcn_readlane(ui, 63);
+        }
+    }
+    Located r;  // not reached for v < NU
+    r.a = p.A;
+    r.na = 0;
+    r.tbase = run;
+    r.ubase = urun;
+    r.ec = 0;
+    r.e_pos = r.e_row = r.e_na = 0;
+    return r;
+}
+
+// The first tile that starts at unit v or later, where v falls in L: in head
+// group h of the entry at offset o, tile o - su clamped to [0, na] (na: the
+// head group's tiles all start before v, so the next head group's first).
+__device__ __forceinline__ long long plan_tile_at(const Plan &P, const Located &L, long long v)
+{
+    const int un = L.na + P.su;
+    const long long loc = v - L.ubase;
+    const int h = (int)(loc / un), o = (int)(loc - (long long)h * un);
+    return L.tbase + (long long)h * L.na + min(max(o - P.su, 0), L.na);
 }
 
 // LDS of one wave: K tile, padded V tile, new key / value (rotated and raw),
@@ -539,10 +592,13 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     pin(vn_sa);
     pin(vn_sh);
     ScanBlock first;
-    const long long NT = plan_total(ent, lane, first);
+    const Totals tot = plan_total(ent, lane, first);
+    const long long NT = tot.NT;
     const int NW = plan_waves(p.NS, NT);
+    const Plan P = make_plan(p, NT, tot.NSEG, NW);
     if (w == 0 && wi == 0) {
-        // the plan's prefix for the merge kernel: tiles before each entry, then NT
+        // the plan's prefix for the merge kernel: units before each entry,
+        // then the totals of tiles and segments
         long long run = 0;
         for (int c0 = 0; c0 < p.A; c0 += 256) {
             ScanBlock sb;
@@ -553,19 +609,31 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int x = c0 + 64 * k + lane;
+                const int ui = units_incl(P, sb, k);
                 if (x < p.A)
-                    p.plan[x] = run + (long long)NHG * (sb.incl[k] - sb.b.na[k]);
-                run += (long long)NHG * __builtin_amdgcn_readlane(sb.incl[k], 63);
+                    p.plan[x] = run + (long long)NHG * (ui - units_of(P, sb.b.na[k]));
+                run += (long long)NHG * __builtin_amdgcn_readlane(ui, 63);
             }
         }
-        if (lane == 0)
-            p.plan[p.A] = run;
+        if (lane == 0) {
+            p.plan[p.A] = NT;
+            p.plan[p.A + 1] = tot.NSEG;
+        }
     }
     STAMP(1, wall_clock64());
     if (w >= NW)
         return;
-    const Plan P = make_plan(p, NT, NW);
-    const long long t0 = plan_t0(P, w), t1 = plan_t0(P, w + 1);
+    // this group's tiles [t0, t1): those that start in its units
+    const long long v0 = plan_v0(P, w);
+    const Located L0 = plan_locate(ent, P, v0, lane, first);
+    const long long t0 = plan_tile_at(P, L0, v0);
+    long long t1 = NT;
+    if (w + 1 < NW) {
+        const long long v1 = plan_v0(P, w + 1);
+        t1 = plan_tile_at(P, plan_locate(ent, P, v1, lane, first), v1);
+    }
+    if (t0 >= t1)
+        return;  // only segment starts in its units
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     using L = WaveLds<D, GCLS>;
@@ -584,10 +652,9 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     const bool ccol = chead < G && (NGRP == 2 || cpart < NPART);
 
     // ---- entry table: lane l holds position, row and tile count of entry ec + l
-    int ec, e_pos, e_row, e_na;
-    int a, h, j, na, row, pos;
-    long long ebase;
-    plan_locate(ent, t0, lane, first, a, ebase, ec, e_pos, e_row, e_na);
+    int ec = L0.ec, e_pos = L0.e_pos, e_row = L0.e_row, e_na = L0.e_na;
+    int a = L0.a, h, j, na, row, pos;
+    long long ebase = L0.tbase;
     auto entry = [&](int e, int &pos_o, int &row_o, int &na_o) {
         if (e < ec || e >= ec + 64) {  // wave-uniform; once per 64 entries
             ec = e & ~63;
@@ -601,11 +668,6 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
         na_o = __shfl(e_na, e - ec, 64);
     };
     entry(a, pos, row, na);
-    {
-        const long long loc = t0 - ebase;
-        h = (int)(loc / na);
-        j = (int)(loc - (long long)h * na);
-    }
 
     // ---- tiles ahead of the current one (a, h, j), h the head group (this
     // wave's kv head is h HG + wi): nxt has its loads in flight while the
@@ -614,7 +676,6 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
         int a, h, j, na, row, pos;
         long long base;
     };
-    TilePos nxt = {a, h, j, na, row, pos, ebase}, nx2 = nxt;
     auto advance = [&](TilePos &x) {  // x := the tile after x
         if (++x.j < x.na)
             return;
@@ -628,6 +689,25 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
             entry(x.a, x.pos, x.row, x.na);
         } while (x.na == 0 && x.a < ent.A);
     };
+    {
+        // t0 is a tile of entry a, or the first of the next valid entry when
+        // v0 fell in the starts of nothing but the entry's last segment's end
+        const long long loc = t0 - ebase;
+        h = (int)(loc / na);
+        j = (int)(loc - (long long)h * na);
+        if (h == NHG) {
+            TilePos x = {a, NHG - 1, na - 1, na, row, pos, ebase};
+            advance(x);
+            a = x.a;
+            h = x.h;
+            j = x.j;
+            na = x.na;
+            row = x.row;
+            pos = x.pos;
+            ebase = x.base;
+        }
+    }
+    TilePos nxt = {a, h, j, na, row, pos, ebase}, nx2 = nxt;
 
     auto seg_base = [&](int srow, int hg, const uint16_t *blk) {
         return (const unsigned char *)(blk + (size_t)srow * p.C * slot + (size_t)(hg * HG + wi) * D);
@@ -1002,7 +1082,7 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
     const int hq = (int)(blockIdx.x % (unsigned)p.Hq), a = (int)(blockIdx.x / (unsigned)p.Hq);
     const int lane = threadIdx.x;
     const int pos = p.positions[a], row = p.rows[a];
-    const long long before = p.plan[a], NT = p.plan[p.A];
+    const long long before = p.plan[a], NT = p.plan[p.A], NSEG = p.plan[p.A + 1];
     uint16_t *out = p.out + a * p.o_sa + hq * p.o_sh;
     if (!entry_valid(p, pos, row)) {
 #pragma unroll
@@ -1015,10 +1095,11 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
     const int G = p.G, h = hq / G, g = hq - h * G, HG = p.HG, NHG = p.NHG;
     const int hg = h / HG, wi = h - hg * HG;  // head group, wave of the group
     const int NW = plan_waves(p.NS, NT);      // NT >= 1: this entry is valid
-    const Plan P = make_plan(p, NT, NW);
+    const Plan P = make_plan(p, NT, NSEG, NW);
     const int na = (pos + kTile) / kTile;
-    const long long ts = before + (long long)hg * na;
-    const int wf = plan_wave_of(P, ts), wl = plan_wave_of(P, ts + na - 1);
+    // the groups that own the segment's first and last tiles, by their units
+    const long long us = before + (long long)hg * units_of(P, na) + P.su;
+    const int wf = plan_wave_of(P, us), wl = plan_wave_of(P, us + na - 1);
     const int ns = wl - wf + 1;
     // partial of group wf + x for this head: (max, sum) and D outputs
     auto slot_of = [&](int x) { return ((size_t)(a * NHG + hg + wf + x) * HG + wi) * G + g; };
@@ -1097,7 +1178,7 @@ __global__ __launch_bounds__(64) void k_decode_merge_wide(DecodeParams p)
     const int hq = (int)(blockIdx.x % (unsigned)p.Hq), a = (int)(blockIdx.x / (unsigned)p.Hq);
     const int lane = threadIdx.x;
     const int pos = p.positions[a], row = p.rows[a];
-    const long long before = p.plan[a], NT = p.plan[p.A];
+    const long long before = p.plan[a], NT = p.plan[p.A], NSEG = p.plan[p.A + 1];
     uint16_t *out = p.out + a * p.o_sa + hq * p.o_sh + lane * PER;
     if (!entry_valid(p, pos, row)) {
 #pragma unroll
@@ -1110,10 +1191,11 @@ __global__ __launch_bounds__(64) void k_decode_merge_wide(DecodeParams p)
     const int G = p.G, h = hq / G, g = hq - h * G, HG = p.HG, NHG = p.NHG;
     const int hg = h / HG, wi = h - hg * HG;  // head group, wave of the group
     const int NW = plan_waves(p.NS, NT);      // NT >= 1: this entry is valid
-    const Plan P = make_plan(p, NT, NW);
+    const Plan P = make_plan(p, NT, NSEG, NW);
     const int na = (pos + kTile) / kTile;
-    const long long ts = before + (long long)hg * na;
-    const int wf = plan_wave_of(P, ts), wl = plan_wave_of(P, ts + na - 1);
+    // the groups that own the segment's first and last tiles, by their units
+    const long long us = before + (long long)hg * units_of(P, na) + P.su;
+    const int wf = plan_wave_of(P, us), wl = plan_wave_of(P, us + na - 1);
     const int ns = wl - wf + 1;
     // the partial of group wf + x for this head sits in slot slot0 + x * step:
     // (max, sum) pairs step apart, outputs step * D floats apart (at most
@@ -1203,7 +1285,7 @@ DecodeWorkspace decode_workspace_layout(int64_t A, int64_t Hq, int64_t Hkv, int6
     w.part_o_off = up(w.qrot_off + (uint64_t)A * Hq * D * 4);
     w.part_ml_off = up(w.part_o_off + slots * D * 4);
     w.plan_off = up(w.part_ml_off + slots * 2 * 4);
-    w.total = up(w.plan_off + ((uint64_t)A + 1) * 8);
+    w.total = up(w.plan_off + ((uint64_t)A + 2) * 8);
     return w;
 }
 

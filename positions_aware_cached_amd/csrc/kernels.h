@@ -25,7 +25,7 @@ struct DecodeParams {
     float *qrot;      // workspace [A, Hq, D]      rotated queries, FP32
     float *part_o;    // workspace [slots, G, D]  per (segment, group, head) unnormalized outputs
     float *part_ml;   // workspace [slots, G, 2]  per (segment, group, head) (max, sum), log2 domain
-    long long *plan;  // workspace [A + 1]: tiles before each entry (x NHG), then the total NT
+    long long *plan;  // workspace [A + 2]: plan units before each entry, then the tile and segment totals
     int32_t *status;  // optional device status word
     int32_t dtype;     // storage type of every 16-bit tensor: 1 BF16, 2 FP16
     int32_t A, S, C, Hq, Hkv, D, G;
