@@ -520,14 +520,15 @@ __device__ Located plan_locate(const Entries &p, const Plan &P, long long v, int
 }
 
 // The first tile that starts at unit v or later, where v falls in L: in head
-// group h of the entry at offset o, tile o - su clamped to [0, na] (na: the
-// head group's tiles all start before v, so the next head group's first).
+// group h of the entry at offset o < na + su, tile max(o - su, 0) of that head
+// group (a segment's start unit comes before its tiles, so it maps to its
+// first tile).
 __device__ __forceinline__ long long plan_tile_at(const Plan &P, const Located &L, long long v)
 {
     const int un = L.na + P.su;
     const long long loc = v - L.ubase;
     const int h = (int)(loc / un), o = (int)(loc - (long long)h * un);
-    return L.tbase + (long long)h * L.na + min(max(o - P.su, 0), L.na);
+    return L.tbase + (long long)h * L.na + max(o - P.su, 0);
 }
 
 // LDS of one wave: K tile, padded V tile, new key / value (rotated and raw),
@@ -623,14 +624,14 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
     STAMP(1, wall_clock64());
     if (w >= NW)
         return;
-    // this group's tiles [t0, t1): those that start in its units
-    const long long v0 = plan_v0(P, w);
+    // this group's tiles [t0, t1): those that start in its units (the units
+    // themselves when they are tiles only)
+    const long long v0 = plan_v0(P, w), v1 = plan_v0(P, w + 1);
     const Located L0 = plan_locate(ent, P, v0, lane, first);
-    const long long t0 = plan_tile_at(P, L0, v0);
-    long long t1 = NT;
-    if (w + 1 < NW) {
-        const long long v1 = plan_v0(P, w + 1);
-        t1 = plan_tile_at(P, plan_locate(ent, P, v1, lane, first), v1);
+    long long t0 = v0, t1 = v1;
+    if (P.su) {
+        t0 = plan_tile_at(P, L0, v0);
+        t1 = w + 1 < NW ? plan_tile_at(P, plan_locate(ent, P, v1, lane, first), v1) : NT;
     }
     if (t0 >= t1)
         return;  // only segment starts in its units
@@ -690,22 +691,9 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
         } while (x.na == 0 && x.a < ent.A);
     };
     {
-        // t0 is a tile of entry a, or the first of the next valid entry when
-        // v0 fell in the starts of nothing but the entry's last segment's end
-        const long long loc = t0 - ebase;
+        const long long loc = t0 - ebase;  // t0 is a tile of entry a
         h = (int)(loc / na);
         j = (int)(loc - (long long)h * na);
-        if (h == NHG) {
-            TilePos x = {a, NHG - 1, na - 1, na, row, pos, ebase};
-            advance(x);
-            a = x.a;
-            h = x.h;
-            j = x.j;
-            na = x.na;
-            row = x.row;
-            pos = x.pos;
-            ebase = x.base;
-        }
     }
     TilePos nxt = {a, h, j, na, row, pos, ebase}, nx2 = nxt;
 
