@@ -65,6 +65,26 @@ def test_edge_positions(D, heads, waves):
     H.check_untouched(run, Kpre, Vpre, list(zip(run.rows_h, run.pos_h)))
 
 
+@pytest.mark.parametrize("case", ["start_only_ranges", "weighted_short_rows"])
+def test_short_rows_unit_plan(case):
+    """Short rows on the device default launch, where the plan counts each
+    segment start as a unit of work: about one unit and a half per group, so
+    some groups own only a segment start and no tile; and short rows with
+    enough tiles for the two-per-unit weighted split."""
+    rng = np.random.default_rng(11 if case == "start_only_ranges" else 12)
+    if case == "start_only_ranges":
+        positions = rng.integers(0, 96, 100)     # 1..3 tiles per row
+    else:
+        positions = rng.integers(0, 640, 200)    # 1..20 tiles per row
+    H.log(f"unit plan {case}: A={len(positions)}")
+    cfg, inp = small_case(128, 32, 8, positions, C=640, seed=len(positions))
+    run = H.DecodeRun(inp, cfg)
+    Kpre, Vpre = run.snapshot()
+    run.run(kernel=0, waves=0)
+    H.full_parity(run, Kpre, Vpre)
+    H.check_untouched(run, Kpre, Vpre, list(zip(run.rows_h, run.pos_h)))
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_readable_edges(D):
     H.log(f"readable edge D={D}")
