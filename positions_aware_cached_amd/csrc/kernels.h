@@ -31,8 +31,8 @@ struct DecodeParams {
     int32_t A, S, C, Hq, Hkv, D, G;
     int32_t NS;        // work groups of the decode launch
     int32_t plan_weighted;  // 1: the launch holds two resident groups per compute unit
-                            // (the first-dispatched half gets more tiles, see plan_t0)
-    int32_t plan_wa, plan_wb;  // tile weights of the first and second half when weighted
+                            // (the first-dispatched half gets more work, see make_plan)
+    int32_t plan_wa, plan_wb;  // work weights of the first and second half when weighted
     int32_t HG, NHG;   // kv heads per group (one wave each), head groups per entry
     float scale_log2;  // log2(e) / sqrt(D)
     float inv_freq[kMaxHalfDim];
