@@ -412,10 +412,11 @@ __device__ __forceinline__ int plan_waves(int launched, long long NT)
 // half gets weight plan_wa, the second plan_wb: v0(w) = floor(W(w) NU /
 // W(NW)), W the running weight.  The host picks the ratio by the work per
 // tile (measured on MI355X with the K/V tiles read non-temporally: 46 : 30
-// with up to 4 query heads per kv head, 41 : 28 with 5-16, the best of the
-// ratios 1.37, 1.46, 1.53 and 1.60 on the Llama-like and long-context
-// batches; with su = 1 the same ratio measured faster than a uniform split on
-// a ragged batch).  The split stays uniform (weight 1 each) when NW is odd or
+// with up to 4 query heads per kv head, the best of the ratios 1.37, 1.46,
+// 1.53 and 1.60 on the Llama-like batch, and with the waves' progress-based
+// priorities also of 42 : 30 - 48 : 30; 45 : 28 with 5-16, against 37 : 28 and
+// 41 : 28 on the long-context batch; with su = 1 the 4-head ratio measured
+// faster than a uniform split on a ragged batch).  The split stays uniform (weight 1 each) when NW is odd or
 // there are fewer than four tiles per group (no range is empty).
 // The plan of a launch, computed once and pinned in scalar registers.
 struct Plan {

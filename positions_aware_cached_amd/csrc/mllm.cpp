@@ -667,9 +667,9 @@ mllm_status decode_impl(mllm_cache *cache, int32_t layer, const mllm_tensor_view
         p.plan = (long long *)((char *)workspace + wl.plan_off);
     }
     p.plan_weighted = waves == 0 && p.NS == 2 * device_cus(d.device) ? 1 : 0;
-    // more query heads per kv head, more work per tile: a smaller lead of the
+    // more query heads per kv head, more work per tile: a different lead of the
     // first-dispatched groups (ratios measured on MI355X)
-    p.plan_wa = G <= 4 ? 46 : 41;
+    p.plan_wa = G <= 4 ? 46 : 45;
     p.plan_wb = G <= 4 ? 30 : 28;
     p.dtype = d.dtype;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
