@@ -1090,13 +1090,29 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
 // lane.
 constexpr int kMergeBatch = 16;
 
+// The merge waves: one per (entry, query head), kMergeWaves to a work group in a
+// one-dimensional grid (the y and z grid sizes are limited).  The waves of a
+// group share nothing; packing them cuts the number of groups the dispatcher
+// has to start, which set the merge's time with thousands of one-wave groups.
+constexpr int kMergeWaves = 4;
+__device__ __forceinline__ bool merge_wave(const DecodeParams &p, int &a, int &hq)
+{
+    const unsigned id = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+    if (id >= (unsigned)p.A * (unsigned)p.Hq)
+        return false;  // the last group's spare waves
+    hq = (int)(id % (unsigned)p.Hq);
+    a = (int)(id / (unsigned)p.Hq);
+    return true;
+}
+
 template <class E, int D>
-__global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
+__global__ __launch_bounds__(64 * kMergeWaves) void k_decode_merge(DecodeParams p)
 {
     constexpr int PER = D / 64;
-    // one-dimensional grid of A * Hq waves (the y and z grid sizes are limited)
-    const int hq = (int)(blockIdx.x % (unsigned)p.Hq), a = (int)(blockIdx.x / (unsigned)p.Hq);
-    const int lane = threadIdx.x;
+    int a, hq;
+    if (!merge_wave(p, a, hq))
+        return;
+    const int lane = threadIdx.x & 63;
     const int pos = p.positions[a], row = p.rows[a];
     const long long before = p.plan[a], NT = p.plan[p.A], NSEG = p.plan[p.A + 1];
     uint16_t *out = p.out + a * p.o_sa + hq * p.o_sh;
@@ -1186,13 +1202,14 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p)
 // constant stride from one base), so a fan-in of 100 takes two trips where
 // the kernel above takes seven.
 template <class E, int D>
-__global__ __launch_bounds__(64) void k_decode_merge_wide(DecodeParams p)
+__global__ __launch_bounds__(64 * kMergeWaves) void k_decode_merge_wide(DecodeParams p)
 {
     constexpr int B = 64, CH = 8;  // groups per round trip, per load chunk
     constexpr int PER = D / 64;  // lane l owns the output dims PER l .. PER l + PER - 1
-    // one-dimensional grid of A * Hq waves (the y and z grid sizes are limited)
-    const int hq = (int)(blockIdx.x % (unsigned)p.Hq), a = (int)(blockIdx.x / (unsigned)p.Hq);
-    const int lane = threadIdx.x;
+    int a, hq;
+    if (!merge_wave(p, a, hq))
+        return;
+    const int lane = threadIdx.x & 63;
     const int pos = p.positions[a], row = p.rows[a];
     const long long before = p.plan[a], NT = p.plan[p.A], NSEG = p.plan[p.A + 1];
     uint16_t *out = p.out + a * p.o_sa + hq * p.o_sh + lane * PER;
@@ -1370,7 +1387,7 @@ hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEve
 template <class E, int D>
 static void launch_merge_d(const DecodeParams &p, hipStream_t stream)
 {
-    const dim3 grid(p.Hq * p.A), block(64);
+    const dim3 grid((p.Hq * p.A + kMergeWaves - 1) / kMergeWaves), block(64 * kMergeWaves);
     if ((long long)p.NS > 12ll * p.A * p.NHG)
         hipLaunchKernelGGL((k_decode_merge_wide<E, D>), grid, block, 0, stream, p);
     else
