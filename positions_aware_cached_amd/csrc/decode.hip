@@ -1090,14 +1090,17 @@ __global__ __launch_bounds__(GCLS == 16 ? 256 : 512, 1) void k_decode_stream(Dec
 // lane.
 constexpr int kMergeBatch = 16;
 
-// The merge waves: one per (entry, query head), kMergeWaves to a work group in a
+// The merge waves: one per (entry, query head), WPG to a work group in a
 // one-dimensional grid (the y and z grid sizes are limited).  The waves of a
-// group share nothing; packing them cuts the number of groups the dispatcher
-// has to start, which set the merge's time with thousands of one-wave groups.
-constexpr int kMergeWaves = 4;
+// group share nothing.  Four to a group for the merge of many rows, where
+// thousands of one-wave groups had to be started; one for the wide merge of
+// a few long rows, whose few waves each wait on many loads and ran slower
+// when four shared a compute unit.
+constexpr int kMergeWaves = 4, kMergeWideWaves = 1;
+template <int WPG>
 __device__ __forceinline__ bool merge_wave(const DecodeParams &p, int &a, int &hq)
 {
-    const unsigned id = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+    const unsigned id = blockIdx.x * WPG + (threadIdx.x >> 6);
     if (id >= (unsigned)p.A * (unsigned)p.Hq)
         return false;  // the last group's spare waves
     hq = (int)(id % (unsigned)p.Hq);
@@ -1110,7 +1113,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_decode_merge(DecodeParams 
 {
     constexpr int PER = D / 64;
     int a, hq;
-    if (!merge_wave(p, a, hq))
+    if (!merge_wave<kMergeWaves>(p, a, hq))
         return;
     const int lane = threadIdx.x & 63;
     const int pos = p.positions[a], row = p.rows[a];
@@ -1202,12 +1205,12 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_decode_merge(DecodeParams 
 // constant stride from one base), so a fan-in of 100 takes two trips where
 // the kernel above takes seven.
 template <class E, int D>
-__global__ __launch_bounds__(64 * kMergeWaves) void k_decode_merge_wide(DecodeParams p)
+__global__ __launch_bounds__(64 * kMergeWideWaves) void k_decode_merge_wide(DecodeParams p)
 {
     constexpr int B = 64, CH = 8;  // groups per round trip, per load chunk
     constexpr int PER = D / 64;  // lane l owns the output dims PER l .. PER l + PER - 1
     int a, hq;
-    if (!merge_wave(p, a, hq))
+    if (!merge_wave<kMergeWideWaves>(p, a, hq))
         return;
     const int lane = threadIdx.x & 63;
     const int pos = p.positions[a], row = p.rows[a];
@@ -1387,11 +1390,14 @@ hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream, hipEve
 template <class E, int D>
 static void launch_merge_d(const DecodeParams &p, hipStream_t stream)
 {
-    const dim3 grid((p.Hq * p.A + kMergeWaves - 1) / kMergeWaves), block(64 * kMergeWaves);
+    const int waves = p.Hq * p.A;
     if ((long long)p.NS > 12ll * p.A * p.NHG)
-        hipLaunchKernelGGL((k_decode_merge_wide<E, D>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((k_decode_merge_wide<E, D>),
+                           dim3((waves + kMergeWideWaves - 1) / kMergeWideWaves),
+                           dim3(64 * kMergeWideWaves), 0, stream, p);
     else
-        hipLaunchKernelGGL((k_decode_merge<E, D>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((k_decode_merge<E, D>), dim3((waves + kMergeWaves - 1) / kMergeWaves),
+                           dim3(64 * kMergeWaves), 0, stream, p);
 }
 
 template <class E>
